@@ -1,0 +1,310 @@
+"""Plain CPU oracle for per-32 microscaled activation quantization and the block-scaled GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import this module.  The product path (the HIP library and its Python binding) never
+imports, links or calls it, and it shares no code, tables or helpers with that path.
+
+Everything here is written to be read against the pages it follows, not to be fast:
+
+* "formats.py" page (the dspark native formats module): module docstring (format contract),
+  FP4_TABLE and constants, e8m0_exponents / e8m0_to_f32, fp4_codes / decode_fp4,
+  e4m3_codes_to_f32 / decode_fp8_block, _log2_ceil_pow2, act_scale, act_quant, act_qdq, exact_in.
+* "hip_quant PKG-INFO" page: "FP8 Formats" table (E4M3 = 1 sign, 4 exponent, 3 mantissa bits,
+  bias 7, max 448, NaN only, round to nearest even) and the BF16 checkpoint helper section
+  (bf16 -> fp32 is exact from the raw bits).
+* "AstrAI commit log" page: the fused-bias commit (bias added in fp32 before the single bf16
+  rounding of the GEMM output).
+
+Decoded values and the GEMM are carried in float64: every decoded value has at most 4
+significant bits times a power of two, so every product of two of them is exact in float64, and
+the float64 sum of K such products is within K * 2^-53 * sum|a*b| of the exact sum.
+
+Readings taken where the pages are silent (each is listed in the design notes as well):
+* The activation floor 1e-4 is the float32 value nearest 1e-4 (the page clamps a float32 tensor).
+* The E8M0 scale output is the byte E + 127 of s = 2^E (the page returns s as float32).
+* A negative value that rounds to zero encodes as 0x80 (negative zero), as the float8_e4m3fn
+  cast the page uses does.
+* The GEMM reference is the unrounded float64 value  sum_k a*b + bias ; the bf16 output is
+  accepted when |out - ref| <= 2^-7 |ref| + 2^-20 sum_k |a*b|.
+* Non-finite activations, NaN E4M3 codes (0x7F, 0xFF) and the NaN scale byte 255 are refused.
+
+No function here is "parity unpinned" except the GEMM below the stated tolerance (the bf16 output
+of any correct implementation may differ from another's inside that bound).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32                      # one scale per 32 consecutive values ("formats.py": BLOCK)
+FP8_MAX = 448.0                 # largest finite E4M3 magnitude ("formats.py": FP8_MAX)
+E8M0_NAN = 255                  # the E8M0 NaN byte ("formats.py": E8M0_NAN)
+E4M3_NAN = (0x7F, 0xFF)         # the two e4m3fn NaN bytes ("formats.py": E4M3_NAN)
+
+# E2M1 code -> value, as printed in "formats.py" (FP4_TABLE): sign is bit 3, code 8 is -0.0.
+FP4_TABLE = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+             -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0)
+
+
+class OracleRefusal(ValueError):
+    """Raised where the pages refuse an input (NaN code, NaN scale, bad shape, non-finite x)."""
+
+
+# ----------------------------------------------------------------------------------------------
+# O1: exact decoders
+# ----------------------------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Raw bf16 bit patterns (uint16) -> float64.
+
+    "hip_quant PKG-INFO", BF16 checkpoint helper: a bf16 pattern is the top 16 bits of the fp32
+    pattern, so widening is exact: fp32 bits = bf16 bits << 16.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e8m0_to_f64(scale_bytes) -> np.ndarray:
+    """E8M0 byte b -> 2^(b - 127); byte 255 (NaN) is refused.
+
+    "formats.py": module docstring (E8M0 scale) and e8m0_exponents / e8m0_to_f32.
+    """
+    s = np.asarray(scale_bytes, dtype=np.uint8)
+    n_nan = int(np.count_nonzero(s == E8M0_NAN))
+    if n_nan:
+        raise OracleRefusal(f"E8M0 scale holds {n_nan} NaN bytes (255)")
+    return np.ldexp(1.0, s.astype(np.int64) - 127)
+
+
+def fp4_unpack(packed) -> np.ndarray:
+    """Packed E2M1 bytes [..., K/2] -> codes [..., K]; byte j holds element 2j in its LOW nibble
+    and element 2j+1 in its HIGH nibble.
+
+    "formats.py": module docstring (MXFP4 layout) and fp4_codes.
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    codes[..., 0::2] = p & 0x0F
+    codes[..., 1::2] = p >> 4
+    return codes
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """E2M1 codes (0..15) -> float64 through the printed table ("formats.py": FP4_TABLE)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if np.any(c > 15):
+        raise OracleRefusal("E2M1 code above 15")
+    return np.asarray(FP4_TABLE, dtype=np.float64)[c]
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """e4m3fn byte -> float64 from its fields; 0x7F and 0xFF (NaN) are refused.
+
+    "hip_quant PKG-INFO", FP8 Formats table: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits, no infinities.  Exponent field 0 is subnormal: m * 2^-9 (= m/8 * 2^(1-7)).
+    Otherwise (1 + m/8) * 2^(e - 7).  "formats.py": e4m3_codes_to_f32 refuses the NaN bytes.
+    """
+    b = np.asarray(codes, dtype=np.uint8)
+    if np.any((b == E4M3_NAN[0]) | (b == E4M3_NAN[1])):
+        raise OracleRefusal("E4M3 operand holds NaN codes (0x7F / 0xFF)")
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = ((b >> 3) & 0xF).astype(np.int64)
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, e - 7))
+    return sign * mag
+
+
+def decode_fp4_rows(packed, scale_bytes) -> np.ndarray:
+    """MXFP4 operand [R, K/2] + E8M0 scales [R, K/32] -> float64 [R, K].
+
+    "formats.py": decode_fp4 -- value = FP4_TABLE[code] * 2^(scale - 127), one scale per 32
+    consecutive K of one row; K must be a multiple of 32 and the scale shape must match.
+    """
+    codes = fp4_unpack(packed)
+    R, K = codes.shape
+    s = np.asarray(scale_bytes, dtype=np.uint8)
+    if K % BLOCK or s.shape != (R, K // BLOCK):
+        raise OracleRefusal(f"fp4 {codes.shape} vs scale {s.shape}")
+    v = e2m1_to_f64(codes).reshape(R, K // BLOCK, BLOCK)
+    return (v * e8m0_to_f64(s)[:, :, None]).reshape(R, K)
+
+
+def decode_e4m3_rows(codes, scale_bytes) -> np.ndarray:
+    """E4M3 activation codes [R, K] + E8M0 scales [R, K/32] (one per 32 K of a row) -> float64.
+
+    This is the value act_qdq stores: q * s ("formats.py": act_qdq).
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    R, K = c.shape
+    s = np.asarray(scale_bytes, dtype=np.uint8)
+    if K % BLOCK or s.shape != (R, K // BLOCK):
+        raise OracleRefusal(f"e4m3 rows {c.shape} vs scale {s.shape}")
+    v = e4m3_to_f64(c).reshape(R, K // BLOCK, BLOCK)
+    return (v * e8m0_to_f64(s)[:, :, None]).reshape(R, K)
+
+
+def decode_fp8_block(codes, scale_bytes) -> np.ndarray:
+    """E4M3 weight [N, K] + E8M0 block scales [ceil(N/32), ceil(K/32)] -> float64 [N, K].
+
+    "formats.py": decode_fp8_block -- one scale per 32x32 block; element (n, k) uses scale
+    [n // 32, k // 32].
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    N, K = c.shape
+    s = np.asarray(scale_bytes, dtype=np.uint8)
+    nb, kb = -(-N // BLOCK), -(-K // BLOCK)
+    if s.shape != (nb, kb):
+        raise OracleRefusal(f"fp8 {c.shape} vs block scale {s.shape}")
+    scale = e8m0_to_f64(s)
+    rows = np.arange(N) // BLOCK
+    cols = np.arange(K) // BLOCK
+    return e4m3_to_f64(c) * scale[rows[:, None], cols[None, :]]
+
+
+# ----------------------------------------------------------------------------------------------
+# O2: act_quant
+# ----------------------------------------------------------------------------------------------
+
+def _e4m3_grid() -> np.ndarray:
+    """The 127 non-negative finite e4m3fn values, indexed by their code 0x00..0x7E (increasing)."""
+    return e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode_rne(y) -> np.ndarray:
+    """Nearest e4m3fn code to each float64 y in [-448, 448], ties to the even code.
+
+    By definition of round-to-nearest-even ("hip_quant PKG-INFO", FP8 Formats: OCP semantics,
+    round to nearest even): take the representable magnitude closest to |y|; on a tie take the
+    one whose code has an even last mantissa bit.  The magnitudes are the 127 codes 0x00..0x7E in
+    increasing order, so the two candidates are found by a sorted search.  The sign bit is the
+    sign of y, zero included (-0 -> 0x80).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(~np.isfinite(y)) or np.any(np.abs(y) > FP8_MAX):
+        raise OracleRefusal("e4m3_encode_rne expects finite |y| <= 448")
+    grid = _e4m3_grid()
+    a = np.abs(y)
+    hi = np.searchsorted(grid, a, side="left")          # grid[hi-1] < a <= grid[hi]
+    hi = np.minimum(hi, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == grid[hi], hi, code).astype(np.uint8)   # exact hits
+    return code | np.where(np.signbit(y), 0x80, 0).astype(np.uint8)
+
+
+def act_scale_bytes(x_bits) -> np.ndarray:
+    """Per-32 E8M0 scale bytes of bf16 activations [..., K] -> uint8 [..., K/32].
+
+    "formats.py": act_scale and _log2_ceil_pow2, step by step, in float32 as the page computes:
+      amax = max over the 32 of |x| (float32), floored at float32(1e-4);
+      t = float32(amax * float32(1/448))  (one float32 multiply, round to nearest even);
+      E = exponent field of t - 127, plus 1 when t's mantissa field is non-zero (ceil of log2 t);
+      the byte is E + 127.
+    K must be a multiple of 32; non-finite activations are refused.
+    """
+    x = bf16_to_f64(x_bits).astype(np.float32)   # exact: bf16 values are float32 values
+    K = x.shape[-1]
+    if K % BLOCK:
+        raise OracleRefusal(f"act_quant: last dim {K} not a multiple of {BLOCK}")
+    if not np.all(np.isfinite(x)):
+        raise OracleRefusal("act_quant: non-finite activation")
+    xb = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK))
+    amax = np.maximum(np.abs(xb).max(axis=-1), np.float32(1e-4))
+    t = (amax * np.float32(1.0 / FP8_MAX)).astype(np.float32)
+    bits = t.view(np.uint32)
+    e = ((bits >> 23) & 0xFF).astype(np.int64) - 127 + ((bits & 0x7FFFFF) != 0)
+    return (e + 127).astype(np.uint8)
+
+
+def act_quant(x_bits) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 activations [..., K] -> (E4M3 codes uint8 [..., K], E8M0 scale bytes uint8 [..., K/32]).
+
+    "formats.py": act_quant -- q = e4m3(clamp(x / s, -448, 448)) with round to nearest even.
+    x / s is exact in float64 (s is a power of two), the clamp keeps |y| <= 448, and the encode
+    is e4m3_encode_rne.
+    """
+    x = bf16_to_f64(x_bits)
+    sb = act_scale_bytes(x_bits)
+    K = x.shape[-1]
+    s = e8m0_to_f64(sb)
+    y = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK)) / s[..., None]
+    y = np.clip(y, -FP8_MAX, FP8_MAX)
+    codes = e4m3_encode_rne(y).reshape(x.shape)
+    return codes, sb
+
+
+def act_qdq_f64(codes, scale_bytes) -> np.ndarray:
+    """q * s as float64 for codes [..., K] and scales [..., K/32] ("formats.py": act_qdq)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    K = c.shape[-1]
+    q = e4m3_to_f64(c).reshape(c.shape[:-1] + (K // BLOCK, BLOCK))
+    return (q * e8m0_to_f64(scale_bytes)[..., None]).reshape(c.shape)
+
+
+def exact_in_bf16(v) -> bool:
+    """Every float64 value of v is a finite bf16 value ("formats.py": exact_in, for bf16).
+
+    A finite float64 is a bf16 value when it survives float64 -> float32 unchanged and its
+    float32 pattern has zero low 16 bits.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)) or np.any(np.abs(v) > float(np.finfo(np.float32).max)):
+        return False
+    f = v.astype(np.float32)
+    if not np.all(np.isfinite(f)) or not np.array_equal(f.astype(np.float64), v):
+        return False
+    return bool(np.all((f.view(np.uint32) & 0xFFFF) == 0))
+
+
+# ----------------------------------------------------------------------------------------------
+# O3: GEMM over exactly decoded operands
+# ----------------------------------------------------------------------------------------------
+
+def gemm_ref(a, b, bias=None) -> tuple[np.ndarray, np.ndarray]:
+    """(ref, S) for C = A . B^T (+ bias): A [..., M, K], B [..., N, K] float64, bias [..., N].
+
+    ref[m, n] = sum_k A[m,k] B[n,k] + bias[n]   and   S[m, n] = sum_k |A[m,k] B[n,k]|.
+    The layout (both operands K-major, output = A times B transposed) is the one the
+    "hip_quant PKG-INFO" page states for its FP8 GEMM and its native MXFP4 call.  The bias is
+    added to the unrounded sum ("AstrAI commit log": bias in fp32 before the one bf16 rounding;
+    here the unrounded float64 value).  The contraction uses the library matmul in float64.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    bt = np.swapaxes(b, -1, -2)
+    ref = a @ bt
+    S = np.abs(a) @ np.abs(bt)
+    if bias is not None:
+        ref = ref + np.asarray(bias, dtype=np.float64)[..., None, :]
+    return ref, S
+
+
+def gemm_ref_at(a, b, rows, cols, bias=None) -> tuple[np.ndarray, np.ndarray]:
+    """(ref, S) of selected outputs (rows[i], cols[i]) only: one dot product each.
+
+    a [M, K], b [N, K] float64 (one batch).  Used to check full-size outputs by sampling.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    prod = a[rows, :] * b[cols, :]
+    ref = prod.sum(axis=1)
+    S = np.abs(prod).sum(axis=1)
+    if bias is not None:
+        ref = ref + np.asarray(bias, dtype=np.float64)[cols]
+    return ref, S
+
+
+def within_tolerance(out_bits, ref, S) -> np.ndarray:
+    """Elementwise acceptance of bf16 outputs: |out - ref| <= 2^-7 |ref| + 2^-20 S.
+
+    out_bits are raw bf16 patterns; a NaN or infinite output is never accepted.
+    """
+    out = bf16_to_f64(out_bits)
+    ref = np.asarray(ref, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    ok = np.abs(out - ref) <= np.ldexp(np.abs(ref), -7) + np.ldexp(S, -20)
+    return ok & np.isfinite(out)
+
