@@ -1,0 +1,158 @@
+"""Python binding of the gfx950 microscaling library (libmx_gfx950.so, C ABI in include/mx.h).
+
+The functions below carry the C ABI's names and only marshal arguments: they take torch tensors
+that already live on the GPU (torch is used for device memory and streams only), pass their
+pointers, sizes and strides to the library and raise on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback of any kind, and loading
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmx_gfx950.so")
+
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_STRIDE, MX_ERR_DEVICE, MX_ERR_LAUNCH = \
+    0, -1, -2, -3, -4, -5, -6
+
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_str(status)})")
+
+
+class MxCaps(ctypes.Structure):
+    _fields_ = [("available", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("compute_units", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("arch", ctypes.c_char * 64), ("reason", ctypes.c_char * 128)]
+
+
+_P, _I = ctypes.c_void_p, ctypes.c_int64
+_SIGS = {
+    "mx_capability": [ctypes.POINTER(MxCaps)],
+    "mx_act_quant": [_P, _P, _P, _I, _I, _P],
+    "mx_act_quant_strided_batched": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
+}
+for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
+    _SIGS[f"mx_gemm_{_n}"] = [_P, _P, _P, _P, _P, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_bias"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_strided_batched"] = [_P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                              _I, _I, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_bias_strided_batched"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                                   _I, _I, _I, _I, _I, _I, _P]
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Loads the built library (raises when it is missing: there is no other implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m block_scaled_precision_act_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, argtypes in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    lib.mx_status_str.argtypes = [ctypes.c_int]
+    lib.mx_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().mx_status_str(status).decode()
+
+
+def mx_capability() -> dict:
+    caps = MxCaps()
+    st = load().mx_capability(ctypes.byref(caps))
+    return {"status": st, "available": bool(caps.available), "device": caps.device,
+            "compute_units": caps.compute_units, "arch": caps.arch.decode(),
+            "reason": caps.reason.decode()}
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(fn: str, st: int):
+    if st != MX_OK:
+        raise MxError(fn, st)
+
+
+def mx_act_quant(x, q, s, stream=None):
+    """x: bf16 [M, K] (cuda); q: uint8 [M, K]; s: uint8 [M, K/32] (written)."""
+    M, K = x.shape[-2], x.shape[-1]
+    _check("mx_act_quant", load().mx_act_quant(_ptr(x), _ptr(q), _ptr(s), M, K, _stream(stream)))
+
+
+def mx_act_quant_strided_batched(x, q, s, stream=None):
+    """x: bf16 [B, M, K]; q: uint8 [B, M, K]; s: uint8 [B, M, K/32]; batch strides from the
+    tensors (a stride-0 x broadcasts)."""
+    B, M, K = x.shape
+    _check("mx_act_quant_strided_batched",
+           load().mx_act_quant_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
+                                               x.stride(0), q.stride(0), s.stride(0),
+                                               _stream(stream)))
+
+
+def _gemm(kind: str, a, a_s, b, b_s, c, bias=None, K=None, stream=None):
+    M, N = c.shape[-2], c.shape[-1]
+    if K is None:
+        K = a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+    lib = load()
+    st = _stream(stream)
+    if c.dim() == 2:
+        if bias is None:
+            r = getattr(lib, f"mx_gemm_{kind}")(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c),
+                                                M, N, K, st)
+        else:
+            r = getattr(lib, f"mx_gemm_{kind}_bias")(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
+                                                     _ptr(bias), _ptr(c), M, N, K, st)
+        name = f"mx_gemm_{kind}" + ("" if bias is None else "_bias")
+    else:
+        B = c.shape[0]
+        strides = [t.stride(0) if t.dim() == 3 else 0 for t in (a, a_s, b, b_s)]
+        if bias is None:
+            r = getattr(lib, f"mx_gemm_{kind}_strided_batched")(
+                _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c), M, N, K, B, *strides,
+                c.stride(0), st)
+            name = f"mx_gemm_{kind}_strided_batched"
+        else:
+            sbias = bias.stride(0) if bias.dim() == 2 else 0
+            r = getattr(lib, f"mx_gemm_{kind}_bias_strided_batched")(
+                _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), _ptr(c), M, N, K, B,
+                *strides, sbias, c.stride(0), st)
+            name = f"mx_gemm_{kind}_bias_strided_batched"
+    _check(name, r)
+
+
+def mx_gemm_fp8_fp4(a, a_s, b, b_s, c, bias=None, stream=None):
+    """a: E4M3 [(B,) M, K]; a_s: [(B,) M, K/32]; b: packed E2M1 [(B,) N, K/2]; b_s: [(B,) N, K/32];
+    c: bf16 [(B,) M, N]; bias: bf16 [(B,) N] or None.  A 2-D operand of a batched call is
+    broadcast (stride 0)."""
+    _gemm("fp8_fp4", a, a_s, b, b_s, c, bias, K=a.shape[-1], stream=stream)
+
+
+def mx_gemm_fp8_fp8(a, a_s, b, b_s, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4 with b: E4M3 [(B,) N, K] and b_s: [(B,) ceil(N/32), K/32]."""
+    _gemm("fp8_fp8", a, a_s, b, b_s, c, bias, K=a.shape[-1], stream=stream)
+
+
+def mx_gemm_fp4_fp4(a, a_s, b, b_s, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4 with a: packed E2M1 [(B,) M, K/2]."""
+    _gemm("fp4_fp4", a, a_s, b, b_s, c, bias, K=2 * a.shape[-1], stream=stream)

@@ -1,0 +1,41 @@
+// Internal interface between the C-ABI layer (mx_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mx {
+
+// Operand encodings, numbered as the scaled f8f6f4 MFMA's format fields number them.
+enum OperandFmt : int { kFp8 = 0, kFp4 = 4 };
+
+// One validated GEMM problem.  Per-matrix element counts are < 2^31; batch strides are in
+// elements of each buffer (bytes for codes / packed / scales, bf16 elements for bias and c).
+struct GemmProblem {
+  const uint8_t* a;
+  const uint8_t* a_s;
+  const uint8_t* b;
+  const uint8_t* b_s;
+  const uint16_t* bias;   // nullptr: no bias
+  uint16_t* c;
+  int M, N, K, batch;
+  int64_t stride_a, stride_as, stride_b, stride_bs, stride_bias, stride_c;
+};
+
+struct DeviceInfo {
+  int device;
+  int cu_count;
+  bool gfx950;
+};
+
+// Cached per-device properties of the calling thread's current device (false: no device).
+bool current_device(DeviceInfo* info);
+
+hipError_t launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
+                            int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
+                            hipStream_t stream);
+
+hipError_t launch_gemm(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
+                       hipStream_t stream);
+
+}  // namespace mx

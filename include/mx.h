@@ -1,0 +1,170 @@
+/*
+ * mx.h -- C ABI of the gfx950 microscaling library: per-32 activation quantization to
+ * E4M3 + E8M0 and block-scaled GEMMs over E4M3 / E2M1 operands.
+ *
+ * Formats (the "formats.py" page, module docstring and FP4_TABLE; the "hip_quant PKG-INFO"
+ * page, FP8 Formats table and native MXFP4 section):
+ *   E4M3  one byte per value, e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no
+ *         infinities, 0x7F / 0xFF are NaN, largest finite 448, subnormals m * 2^-9.
+ *   E2M1  4 bits per value, two per byte: byte j of a row holds element 2j in its LOW nibble
+ *         and element 2j+1 in its HIGH nibble; code -> {0,.5,1,1.5,2,3,4,6}, bit 3 = sign.
+ *   E8M0  one byte b per scale, value 2^(b-127); 255 is NaN.
+ *   bf16  raw 16-bit patterns (the top half of an fp32).
+ *
+ * Conventions shared by every entry point
+ *   - All buffers are device memory owned by the caller; the library never allocates, frees or
+ *     synchronizes.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Row-major, contiguous rows.  GEMMs are "NT": C[M,N] = A[M,K] . B[N,K]^T, both operands
+ *     K-major (the layout the "hip_quant PKG-INFO" page states for its FP8 linear and its
+ *     native MXFP4 call).
+ *   - K must be a positive multiple of 32 (one scale per 32 consecutive K; the "formats.py"
+ *     act_scale refuses other K).  M, N and batch may be any value >= 0; when M, N or batch is 0
+ *     the call returns MX_OK and enqueues nothing.
+ *   - The code / packed operand base pointers (x, q, a, b) must be 16-byte aligned; scale,
+ *     bias and output pointers need no alignment.  Batch strides of the 16-byte-aligned
+ *     operands must keep every batch 16-byte aligned.
+ *   - Strides are counted in elements of each buffer: bytes for code, packed and scale buffers,
+ *     bf16 elements for c, x and bias.  A stride of 0 broadcasts one input to every batch; an
+ *     output stride of 0 with batch > 1 is refused.
+ *   - Each matrix (one batch) must hold fewer than 2^31 elements; batch <= 65535.
+ *   - Argument errors are returned before any HIP call.  A launch failure is reported as
+ *     MX_ERR_LAUNCH; faults inside a kernel surface at the caller's next synchronization.
+ *   - Inputs the formats refuse are outside the contract and are NOT checked on the device:
+ *     NaN E4M3 codes, scale byte 255, non-finite activations.  Their outputs are unspecified.
+ *   - All entry points are thread-safe and stateless apart from a per-device capability cache.
+ */
+#ifndef MX_H_
+#define MX_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MX_OK = 0,
+  MX_ERR_NULL = -1,    /* a required pointer is NULL (or caps == NULL)                       */
+  MX_ERR_SHAPE = -2,   /* K not a positive multiple of 32, a negative size, too large a size */
+  MX_ERR_ALIGN = -3,   /* an operand base or batch stride breaks 16-byte alignment           */
+  MX_ERR_STRIDE = -4,  /* negative stride, or output stride 0 with batch > 1                 */
+  MX_ERR_DEVICE = -5,  /* no HIP device, or the current device is not gfx950                 */
+  MX_ERR_LAUNCH = -6   /* the kernel launch itself failed                                    */
+};
+
+typedef struct mx_caps {
+  int32_t available;      /* 1 when the current device is gfx950 and the kernels can run     */
+  int32_t device;         /* current HIP device ordinal, -1 when there is none               */
+  int32_t compute_units;  /* CUs of the current device, 0 when there is none                 */
+  int32_t reserved;
+  char arch[64];          /* gcnArchName of the current device, "" when there is none         */
+  char reason[128];       /* why `available` is 0, "" otherwise                               */
+} mx_caps;
+
+/* Fills *caps for the calling thread's current device.  Safe to call without any GPU (the
+ * "hip_quant PKG-INFO" page's native MXFP4 section asks the same of its capability query).
+ * Returns MX_OK when the kernels can run, MX_ERR_DEVICE when they cannot, MX_ERR_NULL when
+ * caps is NULL. */
+int mx_capability(mx_caps* caps);
+
+/* Static English text for a status code (never NULL). */
+const char* mx_status_str(int status);
+
+/* ---------------------------------------------------------------------------------------------
+ * act_quant -- the "formats.py" page, act_scale + act_quant (with _log2_ceil_pow2), per 32
+ * consecutive elements of each row:
+ *   amax = max(max |x|, fp32(1e-4))                        in fp32
+ *   E    = ceil(log2(fp32(amax * fp32(1/448))))             from the fp32 exponent bits
+ *   q    = e4m3_rne(clamp(x * 2^-E, -448, 448))              round to nearest even
+ * x  : bf16 [M, K]           (16-byte aligned)
+ * q  : E4M3 codes [M, K]     (16-byte aligned; written)
+ * s  : E8M0 bytes [M, K/32]  (the byte E + 127; written)
+ * The result is bit-exact: every code and scale byte is defined by the steps above.
+ * ------------------------------------------------------------------------------------------- */
+int mx_act_quant(const void* x, void* q, void* s, int64_t M, int64_t K, void* stream);
+
+/* `batch` independent [M, K] problems; batch i reads x + i*stride_x (bf16 elements) and writes
+ * q + i*stride_q and s + i*stride_s (bytes).  stride_q and stride_s must not be 0 when
+ * batch > 1. */
+int mx_act_quant_strided_batched(const void* x, void* q, void* s, int64_t M, int64_t K,
+                                 int64_t batch, int64_t stride_x, int64_t stride_q,
+                                 int64_t stride_s, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Block-scaled GEMM: C[m,n] = bf16_rne( sum_k A[m,k] B[n,k] + bias[n] ), the sum accumulated
+ * in fp32 on the matrix cores, the bias (when given) added in fp32 before the one bf16
+ * rounding (the "AstrAI commit log" page, fused-bias commit).  Decoded operands:
+ *   A[m,k] = e4m3(a[m,k]) * 2^(a_scale[m, k/32] - 127)                    (fp8 A)
+ *   A[m,k] = e2m1(nibble k of a[m, :]) * 2^(a_scale[m, k/32] - 127)       (fp4 A)
+ *   B[n,k] = e2m1(nibble k of b[n, :]) * 2^(b_scale[n, k/32] - 127)       (fp4 B, MXFP4)
+ *   B[n,k] = e4m3(b[n,k]) * 2^(b_scale[n/32, k/32] - 127)                 (fp8 B, 32x32 blocks)
+ * ("formats.py": decode_fp4, decode_fp8_block; act_qdq for the activation side.)
+ * Buffers:
+ *   a       fp8: [M, K] bytes;  fp4: [M, K/2] bytes           (16-byte aligned)
+ *   a_scale [M, K/32] bytes
+ *   b       fp4: [N, K/2] bytes; fp8: [N, K] bytes            (16-byte aligned)
+ *   b_scale fp4: [N, K/32] bytes; fp8: [ceil(N/32), K/32] bytes
+ *   bias    bf16 [N]   (the _bias variants only; must not be NULL there)
+ *   c       bf16 [M, N] (written)
+ * Accuracy: each output satisfies |c - ref| <= 2^-7 |ref| + 2^-20 sum_k |A[m,k] B[n,k]|
+ * against the exact ref = sum_k A B + bias, for inputs whose scaled products stay within fp32
+ * range.
+ * ------------------------------------------------------------------------------------------- */
+int mx_gemm_fp8_fp4(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                    void* c, int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp8_fp4_bias(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                         const void* bias, void* c, int64_t M, int64_t N, int64_t K,
+                         void* stream);
+int mx_gemm_fp8_fp4_strided_batched(const void* a, const void* a_scale, const void* b,
+                                    const void* b_scale, void* c, int64_t M, int64_t N, int64_t K,
+                                    int64_t batch, int64_t stride_a, int64_t stride_a_scale,
+                                    int64_t stride_b, int64_t stride_b_scale, int64_t stride_c,
+                                    void* stream);
+int mx_gemm_fp8_fp4_bias_strided_batched(const void* a, const void* a_scale, const void* b,
+                                         const void* b_scale, const void* bias, void* c,
+                                         int64_t M, int64_t N, int64_t K, int64_t batch,
+                                         int64_t stride_a, int64_t stride_a_scale,
+                                         int64_t stride_b, int64_t stride_b_scale,
+                                         int64_t stride_bias, int64_t stride_c, void* stream);
+
+int mx_gemm_fp8_fp8(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                    void* c, int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp8_fp8_bias(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                         const void* bias, void* c, int64_t M, int64_t N, int64_t K,
+                         void* stream);
+int mx_gemm_fp8_fp8_strided_batched(const void* a, const void* a_scale, const void* b,
+                                    const void* b_scale, void* c, int64_t M, int64_t N, int64_t K,
+                                    int64_t batch, int64_t stride_a, int64_t stride_a_scale,
+                                    int64_t stride_b, int64_t stride_b_scale, int64_t stride_c,
+                                    void* stream);
+int mx_gemm_fp8_fp8_bias_strided_batched(const void* a, const void* a_scale, const void* b,
+                                         const void* b_scale, const void* bias, void* c,
+                                         int64_t M, int64_t N, int64_t K, int64_t batch,
+                                         int64_t stride_a, int64_t stride_a_scale,
+                                         int64_t stride_b, int64_t stride_b_scale,
+                                         int64_t stride_bias, int64_t stride_c, void* stream);
+
+/* Both operands MXFP4 (E2M1 + per-row-32 E8M0), as the skinny A4W4 shapes of the
+ * "fp4-gemm README" page (release-gate shapes) need. */
+int mx_gemm_fp4_fp4(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                    void* c, int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp4_fp4_bias(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                         const void* bias, void* c, int64_t M, int64_t N, int64_t K,
+                         void* stream);
+int mx_gemm_fp4_fp4_strided_batched(const void* a, const void* a_scale, const void* b,
+                                    const void* b_scale, void* c, int64_t M, int64_t N, int64_t K,
+                                    int64_t batch, int64_t stride_a, int64_t stride_a_scale,
+                                    int64_t stride_b, int64_t stride_b_scale, int64_t stride_c,
+                                    void* stream);
+int mx_gemm_fp4_fp4_bias_strided_batched(const void* a, const void* a_scale, const void* b,
+                                         const void* b_scale, const void* bias, void* c,
+                                         int64_t M, int64_t N, int64_t K, int64_t batch,
+                                         int64_t stride_a, int64_t stride_a_scale,
+                                         int64_t stride_b, int64_t stride_b_scale,
+                                         int64_t stride_bias, int64_t stride_c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H_ */

@@ -1,0 +1,146 @@
+"""The C ABI on the host, with no GPU: the library loads, exports every symbol include/mx.h
+declares, and every argument error is reported as a status code before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_act_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mx_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        from block_scaled_precision_act_amd import build
+        build.build()
+    return mx.load()
+
+
+def test_header_declares_the_full_boundary():
+    names = _declared()
+    assert "mx_act_quant" in names and "mx_act_quant_strided_batched" in names
+    for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
+        for v in ("", "_bias", "_strided_batched", "_bias_strided_batched"):
+            assert f"mx_gemm_{k}{v}" in names
+    assert "mx_capability" in names and "mx_status_str" in names
+    assert len(names) == 16
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    for name in _declared():
+        if name == "mx_status_str":
+            continue
+        assert name in mx._SIGS or hasattr(mx, name), name
+
+
+def test_status_strings(lib):
+    for st in range(0, -7, -1):
+        s = mx.status_str(st)
+        assert s and s != "unknown status"
+    assert mx.status_str(-99) == "unknown status"
+
+
+def test_capability_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    caps = mx.mx_capability()
+    assert caps["status"] == mx.MX_ERR_DEVICE and not caps["available"]
+    assert caps["reason"]
+    assert lib.mx_capability(None) == mx.MX_ERR_NULL
+
+
+A16 = 1 << 20          # a fake 16-byte-aligned address: never dereferenced by these calls
+
+
+def _aq(lib, x=A16, q=A16, s=A16, M=4, K=64):
+    return lib.mx_act_quant(x, q, s, M, K, None)
+
+
+def test_act_quant_argument_errors(lib):
+    assert _aq(lib, K=48) == mx.MX_ERR_SHAPE
+    assert _aq(lib, K=0) == mx.MX_ERR_SHAPE
+    assert _aq(lib, M=-1) == mx.MX_ERR_SHAPE
+    assert _aq(lib, M=1 << 26, K=64) == mx.MX_ERR_SHAPE       # 2^32 elements in one matrix
+    assert _aq(lib, x=None) == mx.MX_ERR_NULL
+    assert _aq(lib, s=None) == mx.MX_ERR_NULL
+    assert _aq(lib, x=A16 + 2) == mx.MX_ERR_ALIGN
+    assert _aq(lib, q=A16 + 8) == mx.MX_ERR_ALIGN
+    assert _aq(lib, x=None, M=0) == mx.MX_OK                 # empty: nothing to do
+    sb = lib.mx_act_quant_strided_batched
+    assert sb(A16, A16, A16, 4, 64, 2, 256, 0, 8, None) == mx.MX_ERR_STRIDE
+    assert sb(A16, A16, A16, 4, 64, 2, 256, 256, 0, None) == mx.MX_ERR_STRIDE
+    assert sb(A16, A16, A16, 4, 64, 2, -1, 256, 8, None) == mx.MX_ERR_STRIDE
+    assert sb(A16, A16, A16, 4, 64, 2, 257, 256, 8, None) == mx.MX_ERR_ALIGN
+    assert sb(A16, A16, A16, 4, 64, 70000, 256, 256, 8, None) == mx.MX_ERR_SHAPE
+    assert sb(A16, A16, A16, 4, 64, 0, 256, 256, 8, None) == mx.MX_OK
+
+
+def test_act_quant_valid_args_without_gpu_report_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _aq(lib) == mx.MX_ERR_DEVICE
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+def test_gemm_argument_errors(lib, kind):
+    g = getattr(lib, f"mx_gemm_{kind}")
+    gb = getattr(lib, f"mx_gemm_{kind}_bias")
+    gs = getattr(lib, f"mx_gemm_{kind}_strided_batched")
+    gbs = getattr(lib, f"mx_gemm_{kind}_bias_strided_batched")
+    ok = (A16, A16, A16, A16, A16, 16, 16, 64, None)
+    assert g(*ok[:7], 48, None) == mx.MX_ERR_SHAPE
+    assert g(*ok[:5], -1, 16, 64, None) == mx.MX_ERR_SHAPE
+    assert g(*ok[:5], 1 << 16, 1 << 16, 64, None) == mx.MX_ERR_SHAPE   # M*N >= 2^31
+    assert g(None, *ok[1:]) == mx.MX_ERR_NULL
+    assert g(*ok[:4], None, *ok[5:]) == mx.MX_ERR_NULL
+    assert g(A16 + 4, *ok[1:]) == mx.MX_ERR_ALIGN
+    assert g(A16, A16, A16 + 1, *ok[3:]) == mx.MX_ERR_ALIGN
+    assert g(A16, A16 + 1, A16, A16 + 3, A16 + 2, 16, 16, 64, None) != mx.MX_ERR_ALIGN
+    assert gb(A16, A16, A16, A16, None, A16, 16, 16, 64, None) == mx.MX_ERR_NULL
+    assert g(None, None, None, None, None, 0, 16, 64, None) == mx.MX_OK
+    assert g(None, None, None, None, None, 16, 0, 64, None) == mx.MX_OK
+    args = (A16, A16, A16, A16, A16, 16, 16, 64)
+    assert gs(*args, 2, 1024, 32, 1024, 32, 0, None) == mx.MX_ERR_STRIDE      # output stride 0
+    assert gs(*args, 2, 1024, 32, 1024, 32, -256, None) == mx.MX_ERR_STRIDE
+    assert gs(*args, 2, 1000, 32, 1024, 32, 256, None) == mx.MX_ERR_ALIGN     # A batch not 16B
+    assert gs(*args, 0, 1024, 32, 1024, 32, 256, None) == mx.MX_OK
+    assert gs(*args, 70000, 1024, 32, 1024, 32, 256, None) == mx.MX_ERR_SHAPE
+    bargs = (A16, A16, A16, A16, A16, A16, 16, 16, 64)
+    assert gbs(*bargs, 2, 1024, 32, 1024, 32, -1, 256, None) == mx.MX_ERR_STRIDE
+    assert gbs(A16, A16, A16, A16, None, A16, 16, 16, 64, 2, 0, 0, 0, 0, 0, 256, None) == \
+        mx.MX_ERR_NULL
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+def test_gemm_valid_args_without_gpu_report_device(lib, kind):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    g = getattr(lib, f"mx_gemm_{kind}")
+    assert g(A16, A16, A16, A16, A16, 16, 16, 64, None) == mx.MX_ERR_DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = mx._lib
+    try:
+        mx._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            mx.load(str(tmp_path / "missing.so"))
+    finally:
+        mx._lib = saved
