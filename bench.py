@@ -1,0 +1,250 @@
+"""Benchmark of the microscaled hot path on one MI355X.
+
+One step is the whole path on one batch of synthetic input, back to back on one stream:
+act_quant of bf16 activations x [4096, 2048] (N(0,1) with 1% of entries x100) into E4M3 codes +
+E8M0 scales, then the FP8 x MXFP4 GEMM against E2M1 weights [7168, 2048] (per-32 E8M0 scales
+118..136) with a fused bf16 bias, bf16 out [4096, 7168].
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+
+Prints one JSON line.  `value` is the GEMM's 2*M*N*K flops divided by the time of a whole step
+(act_quant included), in TFLOP/s.  `roofline` is the dominant kernel (the GEMM), timed with HIP
+events on the stream it runs on.  `act_quant` reports the standalone producer on [16384, 7168]
+against HBM bandwidth.  `cpu_baseline` times the oracle on a bounded sample of the same workload
+on the host.  --all adds the GEMM kernel time of the other configurations.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+METRIC = "block-scaled GEMM TFLOP/s (% MFMA peak) + act_quant GB/s (% HBM peak)"
+ACT_QUANT_BYTES_PER_ELEM = 2 + 1 + 1 / 32      # bf16 in, E4M3 code out, one scale byte per 32
+
+
+def _kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, files, per_launch_units: float):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary of `kernel`, when it was
+    taken on the current source (else None)."""
+    p = os.path.join(HERE, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != _kernel_hash(files):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_events(fn, iters, torch):
+    """Average duration of fn() over iters launches, HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record(s)
+        fn()
+        ends[i].record(s)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / iters   # ms
+
+
+def cpu_baseline(w, rows: int):
+    """The oracle as it stands on the first `rows` rows of A (all of N and K)."""
+    from oracle import mx_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    codes, sb = O.act_quant(w.x[:rows])
+    A = O.decode_e4m3_rows(codes, sb)
+    B = O.decode_fp4_rows(w.b, w.b_s)
+    ref, S = O.gemm_ref(A, B, O.bf16_to_f64(w.bias))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"act_quant + decode + float64 GEMM (with sum|a*b|) for rows 0..{rows - 1} of "
+                      f"A [4096, 2048] against all 7168 weight rows; flops counted as 2*{rows}*N*K"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--all", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this hot path has no "
+              f"multi-GPU leg", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_precision_act_amd as mx
+    from block_scaled_precision_act_amd import synth
+
+    mx.load()
+    caps = mx.mx_capability()
+    if not caps["available"]:
+        print(f"no gfx950 device: {caps['reason']}", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    def dev_u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    # ---- the step: act_quant -> FP8 x MXFP4 GEMM + bias on [4096, 2048] x [7168, 2048]
+    w = synth.fp8xmxfp4_4096x7168x2048_bias()
+    M, N, K = w.M, w.N, w.K
+    x = dev_bf16(w.x)
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    b, b_s, bias = dev_u8(w.b), dev_u8(w.b_s), dev_bf16(w.bias)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mx.mx_act_quant(x, q, s, stream=stream)
+        mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mx.mx_act_quant(x, q, s, stream=stream)
+        ev[i][0].record(stream)
+        mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gemm_ms = sum(a.elapsed_time(bb) for a, bb in ev) / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    gemm_files = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip"]
+    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2),
+                "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / MFMA_PEAK_TFLOPS["bf16"], 4),
+                "traffic": _traffic("gemm_fp8_fp4_4096x7168x2048", gemm_files, 1),
+                "kernel": "gemm_bf16_kernel<fp8, fp4, bias> (E4M3/E2M1 decoded exactly to bf16, "
+                          "bf16 MFMA)", "avg_launch_ms": round(gemm_ms, 5),
+                "algorithmic_flops_per_launch": flops}
+
+    # ---- standalone act_quant on [16384, 7168]
+    xs_bits = synth.act_quant_standalone_16384x7168()
+    xs = dev_bf16(xs_bits)
+    del xs_bits
+    qs = torch.empty(xs.shape, dtype=torch.uint8, device="cuda")
+    ss = torch.empty((xs.shape[0], xs.shape[1] // 32), dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        mx.mx_act_quant(xs, qs, ss, stream=stream)
+    aq_ms = time_events(lambda: mx.mx_act_quant(xs, qs, ss, stream=stream), 50, torch)
+    aq_bytes = ACT_QUANT_BYTES_PER_ELEM * xs.numel()
+    aq_gbs = aq_bytes / (aq_ms * 1e-3) / 1e9
+    act_quant = {"workload": "act_quant bf16 [16384, 7168] -> E4M3 + E8M0",
+                 "value": round(aq_gbs, 1), "unit": "GB/s", "avg_launch_ms": round(aq_ms, 5),
+                 "roofline": {"bound": "hbm", "achieved": round(aq_gbs, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(aq_gbs / HBM_PEAK_GBS, 4),
+                              "traffic": _traffic("act_quant_16384x7168",
+                                                  ["block_scaled_precision_act_amd/csrc/act_quant.hip"],
+                                                  1),
+                              "algorithmic_bytes_per_launch": aq_bytes}}
+    del xs, qs, ss
+
+    others = None
+    if args.all:
+        others = bench_others(mx, synth, torch, dev_u8, dev_bf16, stream)
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "e4m3xe2m1->bf16 mfma, f32 acc",
+           "data": "synthetic (seeded numpy PCG64; no dataset)",
+           "config": {"workload": "act_quant x[4096,2048] -> FP8xMXFP4 GEMM 4096x7168x2048 + bias",
+                      "M": M, "N": N, "K": K, "x_outliers": "1% x100",
+                      "weight_scales": "E8M0 118..136", "parallelism": "single GPU"},
+           "roofline": roofline, "act_quant": act_quant,
+           "gemm_only_tflops": round(gemm_tflops, 2)}
+    if others is not None:
+        out["other_configs"] = others
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
+    """GEMM kernel time of the other configurations (operands already quantized in HBM)."""
+    from oracle import mx_oracle  # noqa: F401  (not used for timing)
+    res = {}
+
+    def run(w, kind, bias=True):
+        if w.a_kind == "acts":
+            xq = dev_bf16(w.x)
+            shape = xq.shape
+            a = torch.empty(shape, dtype=torch.uint8, device="cuda")
+            a_s = torch.empty(shape[:-1] + (shape[-1] // 32,), dtype=torch.uint8, device="cuda")
+            if xq.dim() == 3:
+                mx.mx_act_quant_strided_batched(xq, a, a_s, stream=stream)
+            else:
+                mx.mx_act_quant(xq, a, a_s, stream=stream)
+            del xq
+        else:
+            a, a_s = dev_u8(w.a), dev_u8(w.a_s)
+        b, b_s = dev_u8(w.b), dev_u8(w.b_s)
+        bias_t = dev_bf16(w.bias) if (bias and w.bias is not None) else None
+        shape = (w.M, w.N) if w.batch is None else (w.batch, w.M, w.N)
+        c = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        fn = getattr(mx, f"mx_gemm_{kind}")
+        for _ in range(3):
+            fn(a, a_s, b, b_s, c, bias=bias_t, stream=stream)
+        ms = time_events(lambda: fn(a, a_s, b, b_s, c, bias=bias_t, stream=stream), 20, torch)
+        flops = 2.0 * w.M * w.N * w.K * (w.batch or 1)
+        return {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+
+    res["fp8xmxfp4_16x256x512"] = run(synth.fp8xmxfp4_16x256x512(), "fp8_fp4")
+    res["fp8xfp8_1024^3_bias"] = run(synth.fp8xfp8_1024cubed_bias(), "fp8_fp8")
+    for i in range(3):
+        w = synth.a4w4_skinny(i)
+        r = run(w, "fp4_fp4")
+        nbytes = w.M * w.K / 2 + w.M * w.K / 32 + w.N * w.K / 2 + w.N * w.K / 32 + 2 * w.M * w.N
+        r["gbs"] = round(nbytes / (r["ms"] * 1e-3) / 1e9, 1)
+        res[w.name] = r
+    res["fp8xfp8_8x1024x2048x2048"] = run(synth.fp8xfp8_batched_8x1024x2048x2048(), "fp8_fp8")
+    res["fp8xfp8_8192^3"] = run(synth.fp8xfp8_8192cubed(), "fp8_fp8")
+    return res
+
+
+if __name__ == "__main__":
+    main()

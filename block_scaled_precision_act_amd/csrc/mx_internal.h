@@ -35,6 +35,13 @@ hipError_t launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M
                             int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
                             hipStream_t stream);
 
+// FP8-operand kinds: exact bf16 decode + bf16 MFMA (gemm_bf16.hip).
+hipError_t launch_gemm_bf16(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
+                            hipStream_t stream);
+// Both operands MXFP4 on the scaled f8f6f4 MFMA (gemm_fp4.hip).
+hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream);
+
+// Picks the kernel for a problem.
 hipError_t launch_gemm(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
                        hipStream_t stream);
 
