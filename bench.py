@@ -6,6 +6,7 @@ E8M0 scales, then the FP8 x MXFP4 GEMM against E2M1 weights [7168, 2048] (per-32
 118..136) with a fused bf16 bias, bf16 out [4096, 7168].
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+    python bench.py --summarize STATS_DIR FETCH_DIR WRITE_DIR   (CPU only; writes profiles/)
 
 Prints one JSON line.  `value` is the GEMM's 2*M*N*K flops divided by the time of a whole step
 (act_quant included), in TFLOP/s.  `roofline` is the dominant kernel (the GEMM), timed with HIP
@@ -33,6 +34,11 @@ METRIC = "block-scaled GEMM TFLOP/s (% MFMA peak) + act_quant GB/s (% HBM peak)"
 ACT_QUANT_BYTES_PER_ELEM = 2 + 1 + 1 / 32      # bf16 in, E4M3 code out, one scale byte per 32
 
 
+GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip"]
+ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip"]
+COPY_BYTES = 1 << 30          # the plain copy used to calibrate the HBM byte counters
+
+
 def _kernel_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -41,7 +47,7 @@ def _kernel_hash(files):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, files, per_launch_units: float):
+def _traffic(kernel: str, files):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary of `kernel`, when it was
     taken on the current source (else None)."""
     p = os.path.join(HERE, "profiles", f"traffic_{kernel}.json")
@@ -93,10 +99,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true")
+    ap.add_argument("--aq-iters", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this hot path has no "
               f"multi-GPU leg", file=sys.stderr)
@@ -153,11 +166,10 @@ def main():
     flops = 2.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    gemm_files = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip"]
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                 "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / MFMA_PEAK_TFLOPS["bf16"], 4),
-                "traffic": _traffic("gemm_fp8_fp4_4096x7168x2048", gemm_files, 1),
+                "traffic": _traffic("gemm_fp8_fp4_4096x7168x2048", GEMM_SOURCES),
                 "kernel": "gemm_bf16_kernel<fp8, fp4, bias> (E4M3/E2M1 decoded exactly to bf16, "
                           "bf16 MFMA)", "avg_launch_ms": round(gemm_ms, 5),
                 "algorithmic_flops_per_launch": flops}
@@ -170,18 +182,24 @@ def main():
     ss = torch.empty((xs.shape[0], xs.shape[1] // 32), dtype=torch.uint8, device="cuda")
     for _ in range(5):
         mx.mx_act_quant(xs, qs, ss, stream=stream)
-    aq_ms = time_events(lambda: mx.mx_act_quant(xs, qs, ss, stream=stream), 50, torch)
+    aq_ms = time_events(lambda: mx.mx_act_quant(xs, qs, ss, stream=stream), args.aq_iters, torch)
     aq_bytes = ACT_QUANT_BYTES_PER_ELEM * xs.numel()
     aq_gbs = aq_bytes / (aq_ms * 1e-3) / 1e9
     act_quant = {"workload": "act_quant bf16 [16384, 7168] -> E4M3 + E8M0",
                  "value": round(aq_gbs, 1), "unit": "GB/s", "avg_launch_ms": round(aq_ms, 5),
                  "roofline": {"bound": "hbm", "achieved": round(aq_gbs, 1), "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": round(aq_gbs / HBM_PEAK_GBS, 4),
-                              "traffic": _traffic("act_quant_16384x7168",
-                                                  ["block_scaled_precision_act_amd/csrc/act_quant.hip"],
-                                                  1),
+                              "traffic": _traffic("act_quant_16384x7168", ACT_QUANT_SOURCES),
                               "algorithmic_bytes_per_launch": aq_bytes}}
     del xs, qs, ss
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     others = None
     if args.all:
@@ -244,6 +262,105 @@ def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
     res["fp8xfp8_8x1024x2048x2048"] = run(synth.fp8xfp8_batched_8x1024x2048x2048(), "fp8_fp8")
     res["fp8xfp8_8192^3"] = run(synth.fp8xfp8_8192cubed(), "fp8_fp8")
     return res
+
+
+def summarize(stats_dir, fetch_dir, write_dir):
+    """Writes the profiles/ summaries from rocprofv3 CSV output of this script:
+    kernel-trace stats, and FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same counters
+    read for the plain 1 GiB copy (--copy-calibration)."""
+    import csv
+    import glob
+
+    def rows(d, pattern):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    stats = rows(stats_dir, "*kernel_stats.csv")
+    prof = os.path.join(HERE, "profiles")
+    os.makedirs(prof, exist_ok=True)
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
+        return vals
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+
+    def pick(vals, name_part, grid=None):
+        v = [b for (k, g, _), b in vals.items() if name_part in k and (grid is None or g == grid)]
+        return sum(v) / len(v) if v else None
+
+    def calib(vals):
+        # the 1 GiB calibration copy is the copyBuffer dispatch with the largest grid
+        cands = [(g, b) for (k, g, _), b in vals.items() if "copyBuffer" in k]
+        if not cands:
+            return None
+        gmax = max(g for g, _ in cands)
+        v = [b for g, b in cands if g == gmax]
+        return sum(v) / len(v)
+
+    copy_f, copy_w = calib(fetch), calib(write)
+    f_factor = copy_f / COPY_BYTES if copy_f else None
+    w_factor = copy_w / COPY_BYTES if copy_w else None
+    # act_quant on [16384, 7168]: 14336 workgroups of 256 threads
+    aq_grid = 14336 * 256
+    aq_alg = ACT_QUANT_BYTES_PER_ELEM * 16384 * 7168
+    gemm_alg = 4096 * 2048 + 4096 * 64 + 7168 * 1024 + 7168 * 64 + 2 * 7168 + 2 * 4096 * 7168
+    out = {}
+    for name, part, grid, files, alg in (
+            ("act_quant_16384x7168", "act_quant_kernel", aq_grid, ACT_QUANT_SOURCES, aq_alg),
+            ("gemm_fp8_fp4_4096x7168x2048", "gemm_bf16_kernel", None, GEMM_SOURCES, gemm_alg)):
+        f, w = pick(fetch, part, grid), pick(write, part, grid)
+        if f is None or w is None or not f_factor or not w_factor:
+            continue
+        hbm = f / f_factor + w / w_factor
+        out[name] = {"source_hash": _kernel_hash(files), "fetch_bytes_raw": f, "write_bytes_raw": w,
+                     "fetch_scale": f_factor, "write_scale": w_factor,
+                     "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": alg,
+                     "traffic_over_algorithmic": round(hbm / alg, 3)}
+        with open(os.path.join(prof, f"traffic_{name}.json"), "w") as fh:
+            json.dump(out[name], fh, indent=1)
+    cmds = {
+        "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/stats -o run "
+                 "-- python3 bench.py --steps 20 --warmup 5 --no-cpu --aq-iters 20",
+        "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch -o run "
+                 "-- python3 bench.py --steps 2 --warmup 1 --no-cpu --aq-iters 2 --copy-calibration",
+        "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write -o run "
+                 "-- python3 bench.py --steps 2 --warmup 1 --no-cpu --aq-iters 2 --copy-calibration",
+        "summary": "python bench.py --summarize gpurun_out/prof/stats gpurun_out/prof/fetch "
+                   "gpurun_out/prof/write",
+    }
+    lines = ["rocprofv3 kernel-trace statistics of one bench.py run (act_quant x[4096,2048] ->",
+             "FP8xMXFP4 GEMM 4096x7168x2048 + bias, 25 steps; plus 20 standalone act_quant",
+             "launches on x[16384,7168] and 5 warm-up launches of it).", "",
+             "command: " + cmds["stats"], "(run from /tmp as TMPDIR, repository root as cwd)", ""]
+    if stats:
+        keys = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "StdDev", "Percentage"]
+        lines.append(" | ".join(keys))
+        for r in stats:
+            lines.append(" | ".join(str(r.get(k, "")) for k in keys))
+    with open(os.path.join(prof, "kernel_stats_act_quant_and_gemm_fp8_fp4_4096x7168x2048.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    tl = ["HBM traffic per launch from rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE in separate runs),",
+          "each scaled by what the same counter reads for a plain 1 GiB device copy",
+          f"(FETCH_SIZE/bytes = {f_factor}, WRITE_SIZE/bytes = {w_factor}).", "",
+          "commands:", "  " + cmds["fetch"], "  " + cmds["write"], "  " + cmds["summary"], ""]
+    for name, d in out.items():
+        tl.append(f"{name}: hbm_bytes_per_launch = {d['hbm_bytes_per_launch']}, algorithmic = "
+                  f"{d['algorithmic_bytes_per_launch']:.0f}, ratio = {d['traffic_over_algorithmic']} "
+                  f"(fetch {d['fetch_bytes_raw'] / d['fetch_scale']:.0f} B, write "
+                  f"{d['write_bytes_raw'] / d['write_scale']:.0f} B; source hash {d['source_hash']})")
+    with open(os.path.join(prof, "traffic_act_quant_16384x7168_and_gemm_fp8_fp4_4096x7168x2048.txt"), "w") as fh:
+        fh.write("\n".join(tl) + "\n")
+    print("\n".join(lines + [""] + tl))
 
 
 if __name__ == "__main__":
