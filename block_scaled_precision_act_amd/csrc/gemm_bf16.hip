@@ -117,11 +117,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-// Raw codes one thread carries from global memory to LDS for one operand and one K step.
+// Raw codes one thread carries from global memory to LDS for one operand.
 // A row of one K step is FP8: 4 pieces of 16 codes; FP4: 2 pieces of 32 codes (16 bytes each).
 // Thread t owns pieces c = t + i*NT (i < kPer): row c / kPieces, piece c % kPieces.  Rows past
-// the matrix read zeros through the buffer bound; the per-step advance is a scalar offset.
-// Two register sets let the loads of step k+2 fly while step k+1 is decoded into LDS.
+// the matrix and the K half past the end of a partial last step read zeros through the buffer
+// bound; the per-step advance is a scalar offset.  Each piece is decoded into LDS in one part of
+// a K step and reloaded right after, for the step after next, so every piece has a whole K step
+// to arrive with a single register set.
 template <int FMT, int ROWS, int NT>
 struct Stager {
   static constexpr int kPieces = FMT == kFp8 ? 4 : 2;
@@ -132,16 +134,16 @@ struct Stager {
   static constexpr int kRowStride = NT / kPieces;                // rows between pieces i, i+1
   static constexpr int kChunksPerPiece = FMT == kFp8 ? 2 : 4;    // 16-byte bf16 chunks
   static constexpr int kChunks = kPer * kChunksPerPiece;
+  static constexpr uint32_t kOob = 0x80000000u;                  // past any buffer bound
   static_assert(NT % kPieces == 0 && kRowStride % 16 == 0, "swizzle period");
 
   __amdgpu_buffer_rsrc_t codes, scales;
   uint32_t voff[kPer];      // byte offset of piece i at K step 0
   uint32_t soff[kPer];      // byte offset of its scale byte at K step 0
   uint32_t lds0;            // LDS offset (stage-relative) of piece 0's first chunk
-  int koff;                 // K offset of this thread's pieces inside a step
-  bool live;                // thread owns at least piece 0
-  uint4 raw[2][kPer];
-  uint32_t sbyte[2][kPer];
+  bool upper;               // the thread's pieces cover K [32, 64) of a step
+  uint4 raw[kPer];
+  uint32_t sbyte[kPer];
 
   __device__ __forceinline__ void init(const uint8_t* base, const uint8_t* sbase, int row0,
                                        int rows_valid, int K, bool block_scales, int lds_row0) {
@@ -149,8 +151,8 @@ struct Stager {
     const int kb_total = K / 32;
     const int t = threadIdx.x;
     const int p = t % kPieces;
-    koff = (FMT == kFp8 ? 16 : 32) * p;
-    live = kAll || t < kTotal;
+    const int koff = (FMT == kFp8 ? 16 : 32) * p;
+    upper = koff >= 32;
     const int srows = block_scales ? (rows_valid + 31) / 32 : rows_valid;
     codes = make_rsrc(base, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(pitch));
     scales = make_rsrc(sbase, static_cast<uint32_t>(srows) * static_cast<uint32_t>(kb_total));
@@ -164,56 +166,64 @@ struct Stager {
     lds0 = lds_offset(lds_row0 + t / kPieces, kChunksPerPiece * p);
   }
 
-  // PARTIAL: the step holds 32 valid K (the last step when K % 64 == 32).
-  template <bool PARTIAL, int SET>
-  __device__ __forceinline__ void load(int kt) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      raw[SET][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  codes, voff[i], kt * kStepBytes, 0));
-      sbyte[SET][i] = __builtin_amdgcn_raw_buffer_load_b8(scales, soff[i], kt * 2, 0);
-      if (PARTIAL && koff >= 32) raw[SET][i] = make_uint4(0, 0, 0, 0);
-    }
+  // Loads piece I of K step kt; `partial` marks a last step holding only 32 valid K.
+  template <int I>
+  __device__ __forceinline__ void load_piece(int kt, bool partial) {
+    const uint32_t v = (partial && upper) ? kOob : voff[I];
+    raw[I] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(codes, v, kt * kStepBytes, 0));
+    sbyte[I] = __builtin_amdgcn_raw_buffer_load_b8(scales, soff[I], kt * 2, 0);
   }
 
-  // Decodes chunk q (0 <= q < kChunks) of register set SET and writes it to the LDS stage.
-  // The chunks of one piece are consecutive logical chunks of one row: physical chunk of
-  // logical (base + j) is (base ^ swz) ^ j because base is a multiple of kChunksPerPiece.
-  template <int SET, int Q>
+  __device__ __forceinline__ void load_all(int kt, bool partial) {
+    static_for<0, kPer>([&](auto ic) { load_piece<decltype(ic)::value>(kt, partial); });
+  }
+
+  // Part of chunk q when a step's decode is split into 4 parts.
+  static constexpr int part_of(int q) { return (q * 4) / kChunks; }
+
+  // Decodes chunk Q and writes it to the LDS stage.  The chunks of one piece are consecutive
+  // logical chunks of one row: the physical chunk of logical (base + j) is (base ^ swz) ^ j
+  // because base is a multiple of kChunksPerPiece.
+  template <int Q>
   __device__ __forceinline__ void store_chunk(uint8_t* stage) const {
     constexpr int i = Q / kChunksPerPiece, j = Q % kChunksPerPiece;
     if (!kAll && !(static_cast<int>(threadIdx.x) + i * NT < kTotal)) return;
-    const float s = e8m0_value(sbyte[SET][i]);
+    const float s = e8m0_value(sbyte[i]);
     const uint32_t c0 = (lds0 >> 4) & 7;
     uint8_t* dst = stage + (lds0 - (c0 << 4)) + i * kRowStride * kRowBytes + ((c0 ^ j) << 4);
     uint4 o;
     if (FMT == kFp8) {
-      const uint32_t lo = j == 0 ? raw[SET][i].x : raw[SET][i].z;
-      const uint32_t hi = j == 0 ? raw[SET][i].y : raw[SET][i].w;
+      const uint32_t lo = j == 0 ? raw[i].x : raw[i].z;
+      const uint32_t hi = j == 0 ? raw[i].y : raw[i].w;
       o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, false));
       o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, true));
       o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, false));
       o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, true));
     } else {
-      const uint32_t d = j == 0 ? raw[SET][i].x : j == 1 ? raw[SET][i].y : j == 2 ? raw[SET][i].z : raw[SET][i].w;
+      const uint32_t d = j == 0 ? raw[i].x : j == 1 ? raw[i].y : j == 2 ? raw[i].z : raw[i].w;
       o = decode_fp4_dword(d, s);
     }
     *reinterpret_cast<uint4*>(dst) = o;
   }
 
-  // Part PART (of NPARTS) of the decode + store of register set SET: chunks q with
-  // q * NPARTS / kChunks == PART.
-  template <int SET, int PART, int NPARTS>
-  __device__ __forceinline__ void store_part(uint8_t* stage) const {
+  // Part PART of a step's decode + store, then the reload (for step kt) of every piece whose last
+  // chunk was in this part.
+  template <int PART, bool LOAD>
+  __device__ __forceinline__ void store_part_then_load(uint8_t* stage, int kt, bool partial) {
     static_for<0, kChunks>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
-      if constexpr ((q * NPARTS) / kChunks == PART) store_chunk<SET, q>(stage);
+      if constexpr (part_of(q) == PART) store_chunk<q>(stage);
     });
+    if constexpr (LOAD) {
+      static_for<0, kPer>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (part_of(i * kChunksPerPiece + kChunksPerPiece - 1) == PART) load_piece<i>(kt, partial);
+      });
+    }
   }
 
-  template <int SET>
   __device__ __forceinline__ void store_all(uint8_t* stage) const {
-    store_part<SET, 0, 1>(stage);
+    static_for<0, kChunks>([&](auto qc) { store_chunk<decltype(qc)::value>(stage); });
   }
 };
 
@@ -247,16 +257,15 @@ __device__ __forceinline__ void read_frags(const uint8_t* stage, uint32_t a_base
 }
 
 // One K step on LDS stage `cur`: four 16-wide sub-steps.  FRAG_DB: each sub-step reads the next
-// sub-step's fragments ahead of its own MFMAs.  When STORE, the next stage's decode + store rides
-// along: split over the four sub-steps (PARTS == 4) or over the last two (PARTS == 2, when its
-// codes were loaded at the top of this step and need the first half to arrive).  Scheduling
-// groups ask for every MFMA to be followed by a slice of the sub-step's other work, so the matrix
-// pipe keeps issuing while the VALU decodes and the LDS reads and writes proceed; a scheduling
-// fence closes each sub-step so later fragments are not hoisted (and kept live) early.
-template <bool STORE, int SET, int PARTS, bool FRAG_DB, int TM, int TN, class SA, class SB>
+// sub-step's fragments ahead of its own MFMAs.  When STORE, sub-step ks also decodes part ks of
+// the next step's codes into `nxt` and then (LOAD) reloads the finished pieces for step kt_load.
+// Scheduling groups ask for every MFMA to be followed by a slice of the sub-step's other work, so
+// the matrix pipe keeps issuing while the VALU decodes and the LDS reads and writes proceed; a
+// scheduling fence closes each sub-step so later fragments are not hoisted (and kept live) early.
+template <bool STORE, bool LOAD, bool FRAG_DB, int TM, int TN, class SA, class SB>
 __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_t a_base,
                                        uint32_t b_base, const uint32_t (&coff)[4], SA& sa, SB& sb,
-                                       v16f (&acc)[TM][TN]) {
+                                       v16f (&acc)[TM][TN], int kt_load, bool partial_load) {
   Frags<TM, TN> f;
   if constexpr (FRAG_DB) read_frags<TM, TN, 0>(cur, a_base, b_base, coff[0], f);
   static_for<0, 4>([&](auto ksc) {
@@ -273,16 +282,14 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[buf][i], f.b[buf][j],
                                                             acc[i][j], 0, 0, 0);
-    constexpr int part = ks - (4 - PARTS);
-    constexpr bool store_here = STORE && part >= 0;
-    if constexpr (store_here) {
-      sa.template store_part<SET, (part < 0 ? 0 : part), PARTS>(nxt);
-      sb.template store_part<SET, (part < 0 ? 0 : part), PARTS>(nxt);
+    if constexpr (STORE) {
+      sa.template store_part_then_load<ks, LOAD>(nxt, kt_load, partial_load);
+      sb.template store_part_then_load<ks, LOAD>(nxt, kt_load, partial_load);
     }
     // Interleave: each MFMA is followed by a slice of the sub-step's other instructions.
     constexpr int kM = TM * TN;
     constexpr int kReads = FRAG_DB ? (ks < 3 ? TM + TN : 0) : 0;
-    constexpr int kChunksHere = store_here ? (SA::kChunks + PARTS - 1) / PARTS + (SB::kChunks + PARTS - 1) / PARTS : 0;
+    constexpr int kChunksHere = STORE ? (SA::kChunks + 3) / 4 + (SB::kChunks + 3) / 4 : 0;
     constexpr int kCvt = 4 * kChunksHere;
     static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -299,7 +306,7 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
   });
 }
 
-template <int AF, int BF, bool BIAS, int BM, int BN, int WM, int WN, bool FRAG_DB, bool RAW2>
+template <int AF, int BF, bool BIAS, int BM, int BN, int WM, int WN, bool FRAG_DB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;     // WM x WN wavefronts
@@ -338,53 +345,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
 
+  // Pipeline: step k's codes are decoded into LDS stage k & 1 during step k-1's MFMAs, piece by
+  // piece, and each piece is reloaded for step k+1 right after its decode.
   const int KT = (p.K + kBK - 1) / kBK;
   const int last_partial = (p.K % kBK) != 0 ? KT - 1 : -1;
-  auto load = [&](auto setc, int kt) {
-    constexpr int SET = decltype(setc)::value;
-    if (kt == last_partial) { sa.template load<true, SET>(kt); sb.template load<true, SET>(kt); }
-    else { sa.template load<false, SET>(kt); sb.template load<false, SET>(kt); }
-  };
-  if constexpr (RAW2) {
-    // Step k's codes are loaded two steps ahead (register set k & 1), decoded into LDS stage
-    // k & 1 during step k-1's MFMAs, and consumed by step k's MFMAs.
-    load(IntC<0>{}, 0);
-    if (KT > 1) load(IntC<1>{}, 1);
-    sa.template store_all<0>(lds);
-    sb.template store_all<0>(lds);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 2 < KT; kt += 2) {
-      load(IntC<0>{}, kt + 2);
-      k_step<true, 1, 4, FRAG_DB>(lds, lds + kStageBytes, a_base, b_base, coff, sa, sb, acc);
-      __syncthreads();
-      if (kt + 3 < KT) load(IntC<1>{}, kt + 3);
-      k_step<true, 0, 4, FRAG_DB>(lds + kStageBytes, lds, a_base, b_base, coff, sa, sb, acc);
-      __syncthreads();
-    }
-    if (kt + 1 < KT) {
-      k_step<true, 1, 4, FRAG_DB>(lds, lds + kStageBytes, a_base, b_base, coff, sa, sb, acc);
-      __syncthreads();
-      k_step<false, 0, 4, FRAG_DB>(lds + kStageBytes, lds, a_base, b_base, coff, sa, sb, acc);
-    } else {
-      k_step<false, 0, 4, FRAG_DB>(lds, lds + kStageBytes, a_base, b_base, coff, sa, sb, acc);
-    }
-  } else {
-    // Step k+1's codes are loaded at the top of step k and decoded into the other LDS stage
-    // during the second half of step k's MFMAs.
-    load(IntC<0>{}, 0);
-    sa.template store_all<0>(lds);
-    sb.template store_all<0>(lds);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-      load(IntC<0>{}, kt + 1);
-      k_step<true, 0, 2, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes,
-                                  a_base, b_base, coff, sa, sb, acc);
-      __syncthreads();
-    }
-    k_step<false, 0, 2, FRAG_DB>(lds + ((KT - 1) & 1) * kStageBytes, lds, a_base, b_base, coff, sa,
-                                 sb, acc);
+  sa.load_all(0, last_partial == 0);
+  sb.load_all(0, last_partial == 0);
+  sa.store_all(lds);
+  sb.store_all(lds);
+  if (KT > 1) {
+    sa.load_all(1, last_partial == 1);
+    sb.load_all(1, last_partial == 1);
   }
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) {
+    k_step<true, true, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes,
+                                a_base, b_base, coff, sa, sb, acc, kt + 2, kt + 2 == last_partial);
+    __syncthreads();
+  }
+  if (kt + 1 < KT) {
+    k_step<true, false, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes,
+                                 a_base, b_base, coff, sa, sb, acc, 0, false);
+    __syncthreads();
+    ++kt;
+  }
+  k_step<false, false, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds, a_base, b_base, coff, sa, sb,
+                                acc, 0, false);
 
   uint16_t* c = p.c + bz * p.stride_c;
 #pragma unroll
@@ -404,22 +391,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
 }
 
-template <int AF, int BF, int BM, int BN, int WM, int WN, bool FRAG_DB, bool RAW2>
+template <int AF, int BF, int BM, int BN, int WM, int WN, bool FRAG_DB>
 hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c};
   constexpr int kLds = 2 * (BM + BN) * kRowBytes;
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
-  auto k = g.bias ? gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN, FRAG_DB, RAW2>
-                  : gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN, FRAG_DB, RAW2>;
+  auto k = g.bias ? gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN, FRAG_DB>
+                  : gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN, FRAG_DB>;
   // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
   static const hipError_t attr_ok = [] {
     hipError_t e1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN, FRAG_DB, RAW2>),
+        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN, FRAG_DB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     hipError_t e2 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN, FRAG_DB, RAW2>),
+        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN, FRAG_DB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     return e1 != hipSuccess ? e1 : e2;
   }();
@@ -435,9 +422,9 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * g.batch;
   };
-  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 4, 4, true, false>(g, stream);
-  if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2, true, false>(g, stream);
-  return launch_tile<AF, BF, 64, 64, 2, 2, false, false>(g, stream);
+  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 4, 4, true>(g, stream);
+  if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2, true>(g, stream);
+  return launch_tile<AF, BF, 64, 64, 2, 2, false>(g, stream);
 }
 
 }  // namespace
