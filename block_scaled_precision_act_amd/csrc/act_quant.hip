@@ -11,7 +11,8 @@
 // Each lane owns one 16-byte chunk (8 bf16) per step; the four lanes of a DPP quad own one
 // block, so the block max needs two quad permutes and no LDS.  Loads are 16 B, stores of codes
 // are 8 B per lane (512 contiguous bytes per wavefront), the scale byte is written by the
-// quad's first lane.  x * 2^-E is exact (a power-of-two scaling that cannot overflow, and an
+// quad's first lane; code and scale stores are non-temporal (streamed past the caches).
+// x * 2^-E is exact (a power-of-two scaling that cannot overflow, and an
 // underflowing product rounds to a signed zero, as the exact value does), and
 // v_cvt_pk_fp8_f32 rounds to nearest even into OCP e4m3fn with subnormals and signed zero.
 #include "mx_internal.h"
@@ -21,7 +22,6 @@ namespace {
 
 constexpr uint32_t kInv448Bits = 0x3B124925u;   // fp32(1/448)
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;                       // 16-byte chunks per lane per launch slot
 
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's max.
@@ -53,7 +53,9 @@ __device__ __forceinline__ uint32_t encode4(uint32_t lo_pair, uint32_t hi_pair, 
   return static_cast<uint32_t>(r);
 }
 
-// grid.x covers ceil(chunks / (kThreads * kUnroll)) slots, grid.y is the batch index.
+// grid.x covers ceil(chunks / (kThreads * UNROLL)) slots, grid.y is the batch index.
+// UNROLL: 16-byte chunks in flight per lane; NT: non-temporal code and scale stores.
+template <int UNROLL, bool NT>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
     int64_t chunks, int64_t stride_x, int64_t stride_q, int64_t stride_s) {
@@ -61,16 +63,16 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
   const uint4* xv = reinterpret_cast<const uint4*>(x + bz * stride_x);
   uint2* qv = reinterpret_cast<uint2*>(q + bz * stride_q);
   uint8_t* sv = s + bz * stride_s;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * UNROLL) + threadIdx.x;
 
-  uint4 w[kUnroll];
+  uint4 w[UNROLL];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < UNROLL; ++u) {
     const int64_t c = base + u * kThreads;
     w[u] = c < chunks ? xv[c] : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < UNROLL; ++u) {
     const int64_t c = base + u * kThreads;
     // A quad's four chunks are all in range or all out of range (chunks % 4 == 0 and quads
     // start at multiples of 4), so the quad permute below only mixes live lanes.
@@ -83,10 +85,29 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       uint2 codes;
       codes.x = encode4(w[u].x, w[u].y, inv_s);
       codes.y = encode4(w[u].z, w[u].w, inv_s);
-      qv[c] = codes;
-      if ((threadIdx.x & 3) == 0) sv[c >> 2] = static_cast<uint8_t>(byte);
+      if (NT) {
+        __builtin_nontemporal_store(codes.x, reinterpret_cast<uint32_t*>(qv + c));
+        __builtin_nontemporal_store(codes.y, reinterpret_cast<uint32_t*>(qv + c) + 1);
+        if ((threadIdx.x & 3) == 0) __builtin_nontemporal_store(static_cast<uint8_t>(byte), sv + (c >> 2));
+      } else {
+        qv[c] = codes;
+        if ((threadIdx.x & 3) == 0) sv[c >> 2] = static_cast<uint8_t>(byte);
+      }
     }
   }
+}
+
+template <int UNROLL, bool NT>
+hipError_t launch_act_quant_v(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
+                              int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
+                              hipStream_t stream) {
+  const int64_t chunks = M * K / 8;
+  const int64_t per_block = static_cast<int64_t>(kThreads) * UNROLL;
+  const int64_t blocks = (chunks + per_block - 1) / per_block;
+  dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(batch));
+  hipLaunchKernelGGL((act_quant_kernel<UNROLL, NT>), grid, dim3(kThreads), 0, stream, x, q, s,
+                     chunks, stride_x, stride_q, stride_s);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -94,13 +115,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
 hipError_t launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
                             int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
                             hipStream_t stream) {
-  const int64_t chunks = M * K / 8;
-  const int64_t per_block = static_cast<int64_t>(kThreads) * kUnroll;
-  const int64_t blocks = (chunks + per_block - 1) / per_block;
-  dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(batch));
-  hipLaunchKernelGGL(act_quant_kernel, grid, dim3(kThreads), 0, stream, x, q, s, chunks,
-                     stride_x, stride_q, stride_s);
-  return hipGetLastError();
+  // Two 16-byte chunks per lane and non-temporal stores measured best for sustained streaming
+  // (inputs and outputs far larger than the last-level cache).
+  return launch_act_quant_v<2, true>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
 }
 
 }  // namespace mx

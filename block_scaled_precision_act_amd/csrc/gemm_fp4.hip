@@ -110,6 +110,137 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(Args p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Skinny MXFP4 x MXFP4 (small M): v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands.
+// Operand registers of the 16x16x128 scaled MFMA, as measured on gfx950: lane l holds row
+// (l % 16) and K-block g = l / 16 of the 128-wide K step, 16 bytes = 32 E2M1 codes (low nibble
+// first) in dwords 0..3, and passes that block's E8M0 byte; accumulator register r of lane l is
+// C[4 * (l / 16) + r][l % 16].
+// A workgroup owns 16 output columns and all M rows (MT tiles of 16); its W wavefronts split the
+// K steps into contiguous ranges and load a group of up to G steps at once (one memory round
+// trip per group).  The per-wave partial sums are added in LDS in wave order (deterministic),
+// then the bias is added in fp32 and each output is rounded once to bf16.  Rows past M and
+// columns past N read zeros through the buffer bound; K blocks past K read zeros through an
+// out-of-range offset.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+template <int MT, int W, int G, bool BIAS>
+__global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
+  __shared__ v4f red[W][MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t bz = blockIdx.y;
+  const int n0 = blockIdx.x * 16;
+  const int pitch = p.K / 2;
+  const int kb_total = p.K / 32;
+  const int KT = (p.K + 127) / 128;
+
+  const __amdgpu_buffer_rsrc_t ra = rsrc_of(p.a + bz * p.stride_a, static_cast<uint32_t>(p.M) * pitch);
+  const __amdgpu_buffer_rsrc_t ras = rsrc_of(p.a_s + bz * p.stride_as, static_cast<uint32_t>(p.M) * kb_total);
+  const __amdgpu_buffer_rsrc_t rb = rsrc_of(p.b + bz * p.stride_b, static_cast<uint32_t>(p.N) * pitch);
+  const __amdgpu_buffer_rsrc_t rbs = rsrc_of(p.b_s + bz * p.stride_bs, static_cast<uint32_t>(p.N) * kb_total);
+
+  // Byte offsets at K step 0 (rows past the matrix are clamped to the bound: out of range).
+  uint32_t a_off[MT], as_off[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int row = min(16 * t + r16, p.M);
+    a_off[t] = static_cast<uint32_t>(row) * pitch + 16 * g;
+    as_off[t] = static_cast<uint32_t>(row) * kb_total + g;
+  }
+  const int col = min(n0 + r16, p.N);
+  const uint32_t b_off = static_cast<uint32_t>(col) * pitch + 16 * g;
+  const uint32_t bs_off = static_cast<uint32_t>(col) * kb_total + g;
+
+  const int per = (KT + W - 1) / W;
+  const int k_begin = min(wave * per, KT), k_end = min(k_begin + per, KT);
+
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += G) {
+    uint4 av[G][MT], bv[G];
+    uint32_t asv[G][MT], bsv[G];
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      const int kt = k0 + s;
+      const bool live = kt < k_end && kt * 4 + g < kb_total;
+      const uint32_t kbyte = static_cast<uint32_t>(kt) * 64;     // 128 codes = 64 bytes per row
+      const uint32_t kblk = static_cast<uint32_t>(kt) * 4;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        av[s][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ra, live ? a_off[t] : 0x80000000u, kbyte, 0));
+        asv[s][t] = __builtin_amdgcn_raw_buffer_load_b8(ras, live ? as_off[t] : 0x80000000u, kblk, 0);
+      }
+      bv[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rb, live ? b_off : 0x80000000u, kbyte, 0));
+      bsv[s] = __builtin_amdgcn_raw_buffer_load_b8(rbs, live ? bs_off : 0x80000000u, kblk, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      if (k0 + s >= k_end) break;
+      v8i b8 = {static_cast<int>(bv[s].x), static_cast<int>(bv[s].y), static_cast<int>(bv[s].z),
+                static_cast<int>(bv[s].w), 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        v8i a8 = {static_cast<int>(av[s][t].x), static_cast<int>(av[s][t].y),
+                  static_cast<int>(av[s][t].z), static_cast<int>(av[s][t].w), 0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a8, b8, acc[t], kFp4, kFp4, 0, static_cast<int>(asv[s][t]), 0, static_cast<int>(bsv[s]));
+      }
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  // Wave w finishes row tiles t = w, w + W, ...: the partial sums are added in wave order.
+  for (int t = wave; t < MT; t += W) {
+    v4f sum = red[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][t][lane];
+    const int c = n0 + r16;
+    if (c < p.N) {
+      float bias = 0.0f;
+      if (BIAS) bias = __uint_as_float(static_cast<uint32_t>(p.bias[bz * p.stride_bias + c]) << 16);
+      uint16_t* out = p.c + bz * p.stride_c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * t + 4 * g + r;
+        if (row < p.M) out[static_cast<int64_t>(row) * p.N + c] = to_bf16(sum[r] + bias);
+      }
+    }
+  }
+}
+
+template <int MT, int W, int G>
+hipError_t launch_skinny(const GemmProblem& g, hipStream_t stream) {
+  Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
+         g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c};
+  dim3 grid((g.N + 15) / 16, g.batch);
+  if (g.bias)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true>), grid, dim3(64 * W), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, false>), grid, dim3(64 * W), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_skinny_mt(const GemmProblem& g, hipStream_t stream) {
+  const int kt = (g.K + 127) / 128;
+  if (kt >= 32) return launch_skinny<MT, 8, 4>(g, stream);   // long K: 8 wavefronts share it
+  return launch_skinny<MT, 4, 4>(g, stream);
+}
+
 template <int AF, int BF>
 hipError_t launch_formats(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
@@ -125,6 +256,11 @@ hipError_t launch_formats(const GemmProblem& g, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream) {
+  // Skinny problems (M <= 64): 16-column workgroups with split K; otherwise 32x32 wave tiles.
+  if (p.M <= 16) return launch_skinny_mt<1>(p, stream);
+  if (p.M <= 32) return launch_skinny_mt<2>(p, stream);
+  if (p.M <= 48) return launch_skinny_mt<3>(p, stream);
+  if (p.M <= 64) return launch_skinny_mt<4>(p, stream);
   return launch_formats<kFp4, kFp4>(p, stream);
 }
 
