@@ -124,7 +124,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // bound; the per-step advance is a scalar offset.  Each piece is decoded into LDS in one part of
 // a K step and reloaded right after, for the step after next, so every piece has a whole K step
 // to arrive with a single register set.
-template <int FMT, int ROWS, int NT>
+template <int FMT, int ROWS, int NT, int POFF>
 struct Stager {
   static constexpr int kPieces = FMT == kFp8 ? 4 : 2;
   static constexpr int kStepBytes = FMT == kFp8 ? 64 : 32;       // bytes of a row per K step
@@ -171,15 +171,20 @@ struct Stager {
   __device__ __forceinline__ void load_piece(int kt, bool partial) {
     const uint32_t v = (partial && upper) ? kOob : voff[I];
     raw[I] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(codes, v, kt * kStepBytes, 0));
+    __builtin_amdgcn_sched_barrier(0);
     sbyte[I] = __builtin_amdgcn_raw_buffer_load_b8(scales, soff[I], kt * 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   __device__ __forceinline__ void load_all(int kt, bool partial) {
     static_for<0, kPer>([&](auto ic) { load_piece<decltype(ic)::value>(kt, partial); });
   }
 
-  // Part of chunk q when a step's decode is split into 4 parts.
-  static constexpr int part_of(int q) { return (q * 4) / kChunks; }
+  // The quarter of a K step (sub-step) in which piece i is decoded, all its chunks at once; A and
+  // B pieces are offset by POFF so they alternate.  A piece is reloaded at the end of its quarter
+  // and decoded again in the same quarter of the next step: a whole step of latency.
+  static constexpr int piece_part(int i) { return ((i * 4) / kPer + POFF) % 4; }
+  static constexpr int part_of(int q) { return piece_part(q / kChunksPerPiece); }
 
   // Decodes chunk Q and writes it to the LDS stage.  The chunks of one piece are consecutive
   // logical chunks of one row: the physical chunk of logical (base + j) is (base ^ swz) ^ j
@@ -206,20 +211,32 @@ struct Stager {
     *reinterpret_cast<uint4*>(dst) = o;
   }
 
-  // Part PART of a step's decode + store, then the reload (for step kt) of every piece whose last
-  // chunk was in this part.
-  template <int PART, bool LOAD>
-  __device__ __forceinline__ void store_part_then_load(uint8_t* stage, int kt, bool partial) {
+  template <int PART>
+  static constexpr int chunks_in_part() {
+    int n = 0;
+    for (int q = 0; q < kChunks; ++q) n += part_of(q) == PART ? 1 : 0;
+    return n;
+  }
+
+  // Part PART of a step's decode + store.
+  template <int PART>
+  __device__ __forceinline__ void store_part(uint8_t* stage) const {
     static_for<0, kChunks>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       if constexpr (part_of(q) == PART) store_chunk<q>(stage);
     });
-    if constexpr (LOAD) {
-      static_for<0, kPer>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (part_of(i * kChunksPerPiece + kChunksPerPiece - 1) == PART) load_piece<i>(kt, partial);
-      });
-    }
+  }
+
+  // The reloads after part PART: every piece whose last chunk was decoded in that part, in a
+  // fixed order (each load is fenced from the scheduler), so every path into the K loop,
+  // prologue included, leaves the same sequence of outstanding loads and the waits the loop
+  // needs stay as shallow as the data dependences allow.
+  template <int PART>
+  __device__ __forceinline__ void load_part(int kt, bool partial) {
+    static_for<0, kPer>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (piece_part(i) == PART) load_piece<i>(kt, partial);
+    });
   }
 
   __device__ __forceinline__ void store_all(uint8_t* stage) const {
@@ -258,7 +275,8 @@ __device__ __forceinline__ void read_frags(const uint8_t* stage, uint32_t a_base
 
 // One K step on LDS stage `cur`: four 16-wide sub-steps.  FRAG_DB: each sub-step reads the next
 // sub-step's fragments ahead of its own MFMAs.  When STORE, sub-step ks also decodes part ks of
-// the next step's codes into `nxt` and then (LOAD) reloads the finished pieces for step kt_load.
+// the next step's codes into `nxt` and, at its end (LOAD), reloads the finished pieces for step
+// kt_load.
 // Scheduling groups ask for every MFMA to be followed by a slice of the sub-step's other work, so
 // the matrix pipe keeps issuing while the VALU decodes and the LDS reads and writes proceed; a
 // scheduling fence closes each sub-step so later fragments are not hoisted (and kept live) early.
@@ -283,13 +301,13 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[buf][i], f.b[buf][j],
                                                             acc[i][j], 0, 0, 0);
     if constexpr (STORE) {
-      sa.template store_part_then_load<ks, LOAD>(nxt, kt_load, partial_load);
-      sb.template store_part_then_load<ks, LOAD>(nxt, kt_load, partial_load);
+      sa.template store_part<ks>(nxt);
+      sb.template store_part<ks>(nxt);
     }
     // Interleave: each MFMA is followed by a slice of the sub-step's other instructions.
     constexpr int kM = TM * TN;
     constexpr int kReads = FRAG_DB ? (ks < 3 ? TM + TN : 0) : 0;
-    constexpr int kChunksHere = STORE ? (SA::kChunks + 3) / 4 + (SB::kChunks + 3) / 4 : 0;
+    constexpr int kChunksHere = STORE ? SA::template chunks_in_part<ks>() + SB::template chunks_in_part<ks>() : 0;
     constexpr int kCvt = 4 * kChunksHere;
     static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -303,6 +321,10 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
     });
     // Close the scheduling region: later sub-steps' reads must not be hoisted into this one.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (STORE && LOAD) {
+      sa.template load_part<ks>(kt_load, partial_load);
+      sb.template load_part<ks>(kt_load, partial_load);
+    }
   });
 }
 
@@ -326,8 +348,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   const int64_t bz = blockIdx.y;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  Stager<AF, BM, NT> sa;
-  Stager<BF, BN, NT> sb;
+  Stager<AF, BM, NT, 0> sa;
+  Stager<BF, BN, NT, 1> sb;
   sa.init(p.a + bz * p.stride_a, p.a_s + bz * p.stride_as, m0, p.M, p.K, false, 0);
   sb.init(p.b + bz * p.stride_b, p.b_s + bz * p.stride_bs, n0, p.N, p.K, BF == kFp8, BM);
 
@@ -354,8 +376,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   sa.store_all(lds);
   sb.store_all(lds);
   if (KT > 1) {
-    sa.load_all(1, last_partial == 1);
-    sb.load_all(1, last_partial == 1);
+    static_for<0, 4>([&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      sa.template load_part<P>(1, last_partial == 1);
+      sb.template load_part<P>(1, last_partial == 1);
+    });
   }
   __syncthreads();
   int kt = 0;
@@ -422,7 +447,7 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * g.batch;
   };
-  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 4, 4, true>(g, stream);
+  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 4, 2, true>(g, stream);
   if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2, true>(g, stream);
   return launch_tile<AF, BF, 64, 64, 2, 2, false>(g, stream);
 }
