@@ -335,6 +335,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static_assert(BM * BN * 2 <= 2 * kStageBytes, "the bf16 output tile must fit the operand stages");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -398,20 +399,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   k_step<false, false, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds, a_base, b_base, coff, sa, sb,
                                 acc, 0, false);
 
-  uint16_t* c = p.c + bz * p.stride_c;
+  // Epilogue, staged through LDS: fp32 + bias, one bf16 rounding, written into a row-major bf16
+  // tile [BM][BN] (16-byte chunk c of row r at chunk c ^ (4 * bit 2 of r): the two row groups a
+  // wavefront writes in one pass, 4 rows apart, land in different halves of the bank space), then
+  // copied out in coalesced 16-byte row segments.
+  __syncthreads();                       // every wavefront is done reading the operand stages
+  constexpr int kTileRow = BN * 2;       // bytes of one bf16 tile row
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WTN + 32 * j + l32;
-    if (col >= p.N) continue;
+    const int tcol = wn * WTN + 32 * j + l32;
     float bias = 0.0f;
-    if (BIAS) bias = __uint_as_float(static_cast<uint32_t>(p.bias[bz * p.stride_bias + col]) << 16);
+    if (BIAS) {
+      const int col = min(n0 + tcol, p.N - 1);
+      bias = __uint_as_float(static_cast<uint32_t>(p.bias[bz * p.stride_bias + col]) << 16);
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-        if (row < p.M) c[static_cast<int64_t>(row) * p.N + col] = to_bf16(acc[i][j][r] + bias);
+      for (int r = 0; r < 16; r += 2) {
+        const int trow = wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);   // rows trow, trow+1
+        bf16x2 pk = {static_cast<__bf16>(acc[i][j][r] + bias), static_cast<__bf16>(acc[i][j][r + 1] + bias)};
+        const uint32_t w = pk_bits(pk);
+        const int ch = (tcol >> 3) ^ (((trow >> 2) & 1) << 2);
+        const uint32_t off = static_cast<uint32_t>(trow * kTileRow + ch * 16 + (tcol & 7) * 2);
+        *reinterpret_cast<uint16_t*>(lds + off) = static_cast<uint16_t>(w & 0xFFFFu);
+        *reinterpret_cast<uint16_t*>(lds + off + kTileRow) = static_cast<uint16_t>(w >> 16);
       }
+    }
+  }
+  __syncthreads();
+  constexpr int kChunksPerRow = BN / 8;
+  uint16_t* c = p.c + bz * p.stride_c;
+  for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+    const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+    const int row = m0 + trow, col = n0 + tch * 8;
+    if (row >= p.M || col >= p.N) continue;
+    const int ch = tch ^ (((trow >> 2) & 1) << 2);
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
+    uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
+    if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint16_t e[8] = {static_cast<uint16_t>(v.x), static_cast<uint16_t>(v.x >> 16),
+                             static_cast<uint16_t>(v.y), static_cast<uint16_t>(v.y >> 16),
+                             static_cast<uint16_t>(v.z), static_cast<uint16_t>(v.z >> 16),
+                             static_cast<uint16_t>(v.w), static_cast<uint16_t>(v.w >> 16)};
+      for (int k = 0; k < 8 && col + k < p.N; ++k) dst[k] = e[k];
     }
   }
 }
