@@ -37,6 +37,7 @@ ACT_QUANT_BYTES_PER_ELEM = 2 + 1 + 1 / 32      # bf16 in, E4M3 code out, one sca
 GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip"]
 ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip"]
 COPY_BYTES = 1 << 30          # the plain copy used to calibrate the HBM byte counters
+COPY_REPS = 3                 # ... run this many times, last in the program
 
 
 def _kernel_hash(files):
@@ -207,7 +208,7 @@ def main():
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(COPY_REPS):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
@@ -310,12 +311,12 @@ def summarize(stats_dir, fetch_dir, write_dir):
         return sum(v) / len(v) if v else None
 
     def calib(vals):
-        # the 1 GiB calibration copy is the copyBuffer dispatch with the largest grid
-        cands = [(g, b) for (k, g, _), b in vals.items() if "copyBuffer" in k]
-        if not cands:
+        # the calibration copies are the last COPY_REPS copyBuffer dispatches of the run (the
+        # input uploads before them can have the same grid but move fewer bytes)
+        cands = sorted((int(d), b) for (k, _, d), b in vals.items() if "copyBuffer" in k)
+        if len(cands) < COPY_REPS:
             return None
-        gmax = max(g for g, _ in cands)
-        v = [b for g, b in cands if g == gmax]
+        v = [b for _, b in cands[-COPY_REPS:]]
         return sum(v) / len(v)
 
     copy_f, copy_w = calib(fetch), calib(write)
