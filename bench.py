@@ -236,7 +236,6 @@ def main():
 
 def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
     """GEMM kernel time of the other configurations (operands already quantized in HBM)."""
-    from oracle import mx_oracle  # noqa: F401  (not used for timing)
     res = {}
 
     def run(w, kind, bias=True):

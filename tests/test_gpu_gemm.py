@@ -148,6 +148,19 @@ def test_zero_weight_gives_bias_bit_exact(mx, kind):
     assert np.array_equal(out, np.broadcast_to(w.bias, (M, N)))
 
 
+# Wide outputs of 448 tiles of 256x256 with ragged M, N and K edges (1.75 waves on 256 CUs).
+WIDE_CASES = [("acts", "fp4", 500, 57267, 224, None, True),
+               ("acts", "fp8", 256, 57344, 256, 2, False),
+               ("fp8", "fp4", 511, 57300, 96, None, True)]
+
+
+@pytest.mark.parametrize("a_kind,b_kind,M,N,K,batch,with_bias", WIDE_CASES)
+def test_wide_ragged_shapes(mx, a_kind, b_kind, M, N, K, batch, with_bias):
+    w = synth.gemm_inputs(a_kind, b_kind, M, N, K, seed=M + N + K, batch=batch,
+                          with_bias=with_bias)
+    check_workload(mx, w)
+
+
 def test_headline_fp8xmxfp4_16x256x512(mx):
     check_workload(mx, synth.fp8xmxfp4_16x256x512())
 
