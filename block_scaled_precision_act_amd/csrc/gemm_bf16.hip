@@ -13,19 +13,26 @@
 // power of two, so with its E8M0 scale folded in it is EXACTLY a bf16 value; the bf16 MFMA forms
 // exact products and accumulates them in fp32, which meets the bound.
 //
-// Design (per workgroup of 4 wavefronts, tile BM x BN, K step 64):
-//   * global -> registers: 16-byte loads of the raw codes (FP8: 16 values, FP4: 32 values) and the
-//     E8M0 byte of their 32-block, issued one K step ahead of the MFMAs that consume them;
-//   * registers -> LDS: v_cvt_scalef32_pk_bf16_{fp8,fp4} decode two values per instruction with
-//     the scale folded in; rows are 128 B (64 bf16) with the 16-byte chunk index XOR-swizzled by
-//     the row (chunk c of row r lives at c ^ (r & 7)), so the 32 rows one MFMA operand read
-//     touches hit 8 distinct chunk positions per 8 lanes: no bank conflicts;
-//   * two LDS stages, one barrier per K step: the next stage is written while the current one is
-//     read, and the barrier at the end of the step orders both;
-//   * wavefront tile (BM/2) x (BN/2) of 32x32 MFMA blocks held in accumulator registers;
+// Design (per workgroup of WM x WN wavefronts, tile BM x BN, K step 64):
+//   * A is decoded once per workgroup: 16-byte global loads of raw codes and the E8M0 byte of their
+//     32-block go to registers one K step ahead, v_cvt_scalef32_pk_bf16_{fp8,fp4} decode two values
+//     per instruction with the scale folded in, and the bf16 rows (128 B, 16-byte chunks swizzled
+//     by row) are written to an LDS stage;
+//   * B stays raw in LDS (E4M3 or packed E2M1, 64 or 32 bytes per row and K step): every wavefront
+//     reads the raw codes of its own B rows and decodes them in registers.  LDS writes cost about
+//     2.5x what LDS reads cost per byte on gfx950, so staging B raw (1 or 0.5 byte per value instead
+//     of 2) saves more than the decode work it repeats in the WM wavefronts that share a B row;
+//   * K order inside a step: the MFMA's lane group h of sub-step s takes K [32h + 8s, 32h + 8s + 8)
+//     of the step (the same permutation for A and B, so the sum is unchanged).  A lane's four
+//     sub-steps then cover one whole 32-block of its row: one 16- or 32-byte raw read and one scale
+//     per B row and step;
+//   * two LDS stages; the next stage is written in the first three sub-steps, a barrier follows,
+//     and the last sub-step's MFMAs hide the first reads of the next stage;
+//   * wavefront tile (BM/WM) x (BN/WN) of 32x32 MFMA blocks held in accumulator registers;
 //   * the workgroup -> tile map keeps consecutive tiles on one XCD (workgroups are dealt to the 8
-//     XCDs round-robin) and walks them in groups of GROUP_M tile rows, so an XCD's L2 holds the
-//     A rows and B rows its running tiles share.
+//     XCDs round-robin) and walks them in groups of kGroupM tile rows, so an XCD's L2 holds the
+//     A rows and B rows its running tiles share;
+//   * epilogue: fp32 + bias, one RNE rounding, staged through LDS for 16-byte row stores.
 #include "mx_internal.h"
 
 namespace mx {
@@ -48,8 +55,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kBK = 64;          // K elements per stage
-constexpr int kRowBytes = 128;   // one LDS row: 64 bf16
+constexpr int kRowBytes = 128;   // one decoded LDS row: 64 bf16
 constexpr int kGroupM = 8;
+constexpr int kParts = 3;        // sub-steps that stage the next K step (the fourth holds the barrier)
 
 struct Args {
   const uint8_t* a;
@@ -65,24 +73,12 @@ struct Args {
 
 // fp32 value of an E8M0 byte (2^(b-127)); byte 0 is the fp32 subnormal 2^-127.
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
-  return __uint_as_float(b ? (b << 23) : 0x00400000u);
+  return __uint_as_float(max(b << 23, 0x00400000u));
 }
 
 __device__ __forceinline__ uint32_t pk_bits(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// 16 E4M3 codes times s -> 16 bf16 (two 16-byte chunks, element order preserved).
-__device__ __forceinline__ void decode_fp8(uint4 v, float s, uint4& o0, uint4& o1) {
-  o0.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, false));
-  o0.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, s, true));
-  o0.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, s, false));
-  o0.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, s, true));
-  o1.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, s, false));
-  o1.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, s, true));
-  o1.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, s, false));
-  o1.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, s, true));
-}
-
-// 8 E2M1 codes (one dword, low nibble first) times s -> 8 bf16 (one 16-byte chunk).
+// 8 E2M1 codes (one dword, low nibble first) times s -> 8 bf16.
 __device__ __forceinline__ uint4 decode_fp4_dword(uint32_t d, float s) {
   uint4 o;
   o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0));
@@ -92,12 +88,22 @@ __device__ __forceinline__ uint4 decode_fp4_dword(uint32_t d, float s) {
   return o;
 }
 
-// LDS rows are 128 B (64 bf16 = 8 chunks of 16 B).  Chunk c of row r is stored at chunk
+// 8 E4M3 codes (two dwords) times s -> 8 bf16.
+__device__ __forceinline__ uint4 decode_fp8_pair(uint32_t lo, uint32_t hi, float s) {
+  uint4 o;
+  o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, false));
+  o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, true));
+  o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, false));
+  o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, true));
+  return o;
+}
+
+// Decoded rows are 128 B (64 bf16 = 8 chunks of 16 B).  Chunk c of row r is stored at chunk
 // c ^ swz(r), swz(r) = (r & 7) ^ parity(bits 1..3 of r), period 16 in r.  It keeps every LDS pass
-// free of bank conflicts for all three access patterns, whether a pass serves 8 lanes (128 B of
-// banks) or 16 lanes (256 B): the fragment reads (8 or 16 consecutive rows at one logical chunk),
-// the FP8 decode writes (rows r, r+1 x 4 pieces of 2 chunks) and the FP4 decode writes (rows
-// r..r+3 x 2 pieces of 4 chunks).  Found by exhaustive search over period-16 tables.
+// free of bank conflicts, whether a pass serves 8 lanes (128 B of banks) or 16 lanes (256 B), for
+// the fragment reads (8 or 16 consecutive rows at one logical chunk), the FP8 decode writes (rows
+// r, r+1 x 4 pieces of 2 chunks) and the FP4 decode writes (rows r..r+3 x 2 pieces of 4 chunks).
+// Found by exhaustive search over period-16 tables.
 __device__ __forceinline__ int swz(int row) {
   return (row & 7) ^ (__builtin_popcount((row >> 1) & 7) & 1);
 }
@@ -106,9 +112,13 @@ __device__ __forceinline__ uint32_t lds_offset(int row, int chunk) {
   return static_cast<uint32_t>(row * kRowBytes + ((chunk ^ swz(row)) << 4));
 }
 
-__device__ __forceinline__ uint16_t to_bf16(float v) {
-  bf16x2 p = {static_cast<__bf16>(v), static_cast<__bf16>(0.0f)};
-  return static_cast<uint16_t>(pk_bits(p) & 0xFFFFu);
+// Raw code rows hold one K step of one operand row (E4M3: 64 B = 4 units of 16 B; E2M1: 32 B =
+// 2 units).  Unit u of row r is stored at u ^ graw(r).  16 consecutive rows reading one logical
+// unit, and the staging writes (4 rows x 4 units or 8 rows x 2 units per 16 lanes), then touch
+// 16 distinct 16-byte bank groups.  Period 16 in r.
+template <int FMT>
+__device__ __forceinline__ int graw(int row) {
+  return FMT == kFp8 ? (row >> 2) & 3 : (row >> 3) & 1;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -117,14 +127,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-// Raw codes one thread carries from global memory to LDS for one operand.
+// Moves one operand's codes for one K step from global memory into an LDS stage region.
 // A row of one K step is FP8: 4 pieces of 16 codes; FP4: 2 pieces of 32 codes (16 bytes each).
 // Thread t owns pieces c = t + i*NT (i < kPer): row c / kPieces, piece c % kPieces.  Rows past
 // the matrix and the K half past the end of a partial last step read zeros through the buffer
-// bound; the per-step advance is a scalar offset.  Each piece is decoded into LDS in one part of
-// a K step and reloaded right after, for the step after next, so every piece has a whole K step
-// to arrive with a single register set.
-template <int FMT, int ROWS, int NT, int POFF>
+// bound; the per-step advance is a scalar offset.
+// DECODE: each piece is decoded with its E8M0 scale into bf16 chunks of 128-byte rows; otherwise
+// the raw 16 bytes are stored into rows of kStepBytes.
+// Piece i is staged in part PART0 + i * NPART / kPer of a K step and reloaded right after, for
+// the step after next, so every piece has a whole K step to arrive with a single register set.
+template <int FMT, int ROWS, int NT, bool DECODE, int PART0, int NPART>
 struct Stager {
   static constexpr int kPieces = FMT == kFp8 ? 4 : 2;
   static constexpr int kStepBytes = FMT == kFp8 ? 64 : 32;       // bytes of a row per K step
@@ -132,21 +144,22 @@ struct Stager {
   static constexpr int kPer = (kTotal + NT - 1) / NT;
   static constexpr bool kAll = kTotal % NT == 0;
   static constexpr int kRowStride = NT / kPieces;                // rows between pieces i, i+1
-  static constexpr int kChunksPerPiece = FMT == kFp8 ? 2 : 4;    // 16-byte bf16 chunks
+  static constexpr int kChunksPerPiece = DECODE ? (FMT == kFp8 ? 2 : 4) : 1;
   static constexpr int kChunks = kPer * kChunksPerPiece;
   static constexpr uint32_t kOob = 0x80000000u;                  // past any buffer bound
   static_assert(NT % kPieces == 0 && kRowStride % 16 == 0, "swizzle period");
+  static_assert(PART0 >= 0 && PART0 + NPART <= kParts && NPART >= 1, "parts");
 
   __amdgpu_buffer_rsrc_t codes, scales;
   uint32_t voff[kPer];      // byte offset of piece i at K step 0
   uint32_t soff[kPer];      // byte offset of its scale byte at K step 0
-  uint32_t lds0;            // LDS offset (stage-relative) of piece 0's first chunk
+  uint32_t lds0;            // LDS offset (stage-relative) of piece 0
   bool upper;               // the thread's pieces cover K [32, 64) of a step
   uint4 raw[kPer];
   uint32_t sbyte[kPer];
 
   __device__ __forceinline__ void init(const uint8_t* base, const uint8_t* sbase, int row0,
-                                       int rows_valid, int K, bool block_scales, int lds_row0) {
+                                       int rows_valid, int K, bool block_scales, uint32_t region) {
     const int pitch = FMT == kFp8 ? K : K / 2;
     const int kb_total = K / 32;
     const int t = threadIdx.x;
@@ -155,7 +168,8 @@ struct Stager {
     upper = koff >= 32;
     const int srows = block_scales ? (rows_valid + 31) / 32 : rows_valid;
     codes = make_rsrc(base, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(pitch));
-    scales = make_rsrc(sbase, static_cast<uint32_t>(srows) * static_cast<uint32_t>(kb_total));
+    if (DECODE)
+      scales = make_rsrc(sbase, static_cast<uint32_t>(srows) * static_cast<uint32_t>(kb_total));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int r = min(row0 + t / kPieces + i * kRowStride, rows_valid);   // == rows_valid: OOB
@@ -163,7 +177,11 @@ struct Stager {
       const int sr = block_scales ? r / 32 : r;
       soff[i] = static_cast<uint32_t>(sr) * kb_total + koff / 32;
     }
-    lds0 = lds_offset(lds_row0 + t / kPieces, kChunksPerPiece * p);
+    const int lrow = t / kPieces;
+    if (DECODE)
+      lds0 = region + lds_offset(lrow, kChunksPerPiece * p);
+    else
+      lds0 = region + static_cast<uint32_t>(lrow * kStepBytes + ((p ^ graw<FMT>(lrow)) << 4));
   }
 
   // Loads piece I of K step kt; `partial` marks a last step holding only 32 valid K.
@@ -172,43 +190,42 @@ struct Stager {
     const uint32_t v = (partial && upper) ? kOob : voff[I];
     raw[I] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(codes, v, kt * kStepBytes, 0));
     __builtin_amdgcn_sched_barrier(0);
-    sbyte[I] = __builtin_amdgcn_raw_buffer_load_b8(scales, soff[I], kt * 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DECODE) {
+      sbyte[I] = __builtin_amdgcn_raw_buffer_load_b8(scales, soff[I], kt * 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   __device__ __forceinline__ void load_all(int kt, bool partial) {
     static_for<0, kPer>([&](auto ic) { load_piece<decltype(ic)::value>(kt, partial); });
   }
 
-  // The quarter of a K step (sub-step) in which piece i is decoded, all its chunks at once; A and
-  // B pieces are offset by POFF so they alternate.  A piece is reloaded at the end of its quarter
-  // and decoded again in the same quarter of the next step: a whole step of latency.
-  static constexpr int piece_part(int i) { return ((i * 4) / kPer + POFF) % 4; }
+  static constexpr int piece_part(int i) { return PART0 + (i * NPART) / kPer; }
   static constexpr int part_of(int q) { return piece_part(q / kChunksPerPiece); }
 
-  // Decodes chunk Q and writes it to the LDS stage.  The chunks of one piece are consecutive
-  // logical chunks of one row: the physical chunk of logical (base + j) is (base ^ swz) ^ j
-  // because base is a multiple of kChunksPerPiece.
+  // Writes chunk Q (decoded, or the raw piece) to the LDS stage.  The chunks of one decoded piece
+  // are consecutive logical chunks of one row: the physical chunk of logical (base + j) is
+  // (base ^ swz) ^ j because base is a multiple of kChunksPerPiece.  Rows i * kRowStride apart
+  // share the swizzle (period 16).
   template <int Q>
   __device__ __forceinline__ void store_chunk(uint8_t* stage) const {
     constexpr int i = Q / kChunksPerPiece, j = Q % kChunksPerPiece;
     if (!kAll && !(static_cast<int>(threadIdx.x) + i * NT < kTotal)) return;
-    const float s = e8m0_value(sbyte[i]);
-    const uint32_t c0 = (lds0 >> 4) & 7;
-    uint8_t* dst = stage + (lds0 - (c0 << 4)) + i * kRowStride * kRowBytes + ((c0 ^ j) << 4);
-    uint4 o;
-    if (FMT == kFp8) {
-      const uint32_t lo = j == 0 ? raw[i].x : raw[i].z;
-      const uint32_t hi = j == 0 ? raw[i].y : raw[i].w;
-      o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, false));
-      o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, true));
-      o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, false));
-      o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, true));
+    if constexpr (!DECODE) {
+      *reinterpret_cast<uint4*>(stage + lds0 + i * kRowStride * kStepBytes) = raw[i];
     } else {
-      const uint32_t d = j == 0 ? raw[i].x : j == 1 ? raw[i].y : j == 2 ? raw[i].z : raw[i].w;
-      o = decode_fp4_dword(d, s);
+      const float s = e8m0_value(sbyte[i]);
+      const uint32_t c0 = (lds0 >> 4) & 7;
+      uint8_t* dst = stage + (lds0 - (c0 << 4)) + i * kRowStride * kRowBytes + ((c0 ^ j) << 4);
+      uint4 o;
+      if constexpr (FMT == kFp8) {
+        o = j == 0 ? decode_fp8_pair(raw[i].x, raw[i].y, s) : decode_fp8_pair(raw[i].z, raw[i].w, s);
+      } else {
+        const uint32_t d = j == 0 ? raw[i].x : j == 1 ? raw[i].y : j == 2 ? raw[i].z : raw[i].w;
+        o = decode_fp4_dword(d, s);
+      }
+      *reinterpret_cast<uint4*>(dst) = o;
     }
-    *reinterpret_cast<uint4*>(dst) = o;
   }
 
   template <int PART>
@@ -218,19 +235,22 @@ struct Stager {
     return n;
   }
 
-  // Part PART of a step's decode + store.
-  template <int PART>
-  __device__ __forceinline__ void store_part(uint8_t* stage) const {
-    static_for<0, kChunks>([&](auto qc) {
-      constexpr int q = decltype(qc)::value;
-      if constexpr (part_of(q) == PART) store_chunk<q>(stage);
-    });
+  // Index of the N-th chunk staged in part PART.
+  template <int PART, int N>
+  static constexpr int nth_chunk() {
+    int n = 0;
+    for (int q = 0; q < kChunks; ++q) {
+      if (part_of(q) == PART) {
+        if (n == N) return q;
+        ++n;
+      }
+    }
+    return -1;
   }
 
-  // The reloads after part PART: every piece whose last chunk was decoded in that part, in a
-  // fixed order (each load is fenced from the scheduler), so every path into the K loop,
-  // prologue included, leaves the same sequence of outstanding loads and the waits the loop
-  // needs stay as shallow as the data dependences allow.
+  // The reloads after part PART: every piece staged in that part, in a fixed order (each load is
+  // fenced from the scheduler), so every path into the K loop, prologue included, leaves the same
+  // sequence of outstanding loads and the waits the loop needs stay as shallow as the data allow.
   template <int PART>
   __device__ __forceinline__ void load_part(int kt, bool partial) {
     static_for<0, kPer>([&](auto ic) {
@@ -244,7 +264,84 @@ struct Stager {
   }
 };
 
-// Tile coordinates of workgroup `bid` out of `nb`: XCD-contiguous, then grouped by GROUP_M rows.
+// The B operand of one wavefront: TN tiles of 32 rows.  Each step, lane (row l % 32, group h)
+// reads the raw codes of K [32h, 32h+32) of its row from the LDS stage (E4M3: 32 bytes, E2M1: 16
+// bytes) and its E8M0 byte (loaded from global memory one step ahead), and decodes the 8 values of
+// each sub-step into the MFMA's bf16 operand just before they are needed.
+template <int BF, int TN>
+struct BRegs {
+  static constexpr int kQ = BF == kFp8 ? 2 : 1;        // 16-byte units per row per lane
+  static constexpr int kPitch = BF == kFp8 ? 64 : 32;  // raw row bytes per step
+  uint4 raw[TN][kQ];
+  float scale[TN];
+  uint32_t sbyte[TN];           // scale bytes of the step loaded next
+  __amdgpu_buffer_rsrc_t srsrc;
+  uint32_t soff[TN];
+  uint32_t lds_off[kQ];         // stage-relative LDS offset of tile 0
+
+  __device__ __forceinline__ void init(const uint8_t* sbase, int n_first, int N, int K,
+                                       uint32_t region, int row_local) {
+    const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+    const int kb_total = K / 32;
+    const int srows = BF == kFp8 ? (N + 31) / 32 : N;
+    srsrc = make_rsrc(sbase, static_cast<uint32_t>(srows) * static_cast<uint32_t>(kb_total));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n_first + 32 * j + l32;
+      const int sr = min(BF == kFp8 ? n / 32 : n, srows);               // == srows: OOB -> 0
+      soff[j] = static_cast<uint32_t>(sr) * kb_total + h;
+    }
+    const int r = row_local + l32;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int u = BF == kFp8 ? 2 * h + q : h;
+      lds_off[q] = region + static_cast<uint32_t>(r * kPitch + ((u ^ graw<BF>(r)) << 4));
+    }
+  }
+
+  __device__ __forceinline__ void load_scales(int kt) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sbyte[j] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, soff[j], kt * 2, 0);
+  }
+
+  __device__ __forceinline__ void take_scales() {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) scale[j] = e8m0_value(sbyte[j]);
+  }
+
+  template <int J, int Q>
+  __device__ __forceinline__ void read_raw(const uint8_t* stage) {
+    raw[J][Q] = *reinterpret_cast<const uint4*>(stage + lds_off[Q] + 32 * J * kPitch);
+  }
+
+  __device__ __forceinline__ void read_raw_all(const uint8_t* stage) {
+    static_for<0, TN * kQ>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      read_raw<t / kQ, t % kQ>(stage);
+    });
+  }
+
+  // bf16 operand of tile J for sub-step S: K [32h + 8S, 32h + 8S + 8) of the row.
+  template <int S, int J>
+  __device__ __forceinline__ void decode(bf16x8& out) const {
+    uint4 o;
+    if constexpr (BF == kFp8) {
+      const uint4 q = raw[J][S >> 1];
+      o = (S & 1) ? decode_fp8_pair(q.z, q.w, scale[J]) : decode_fp8_pair(q.x, q.y, scale[J]);
+    } else {
+      const uint32_t d = S == 0 ? raw[J][0].x : S == 1 ? raw[J][0].y : S == 2 ? raw[J][0].z : raw[J][0].w;
+      o = decode_fp4_dword(d, scale[J]);
+    }
+    out = __builtin_bit_cast(bf16x8, o);
+  }
+
+  template <int S>
+  __device__ __forceinline__ void decode_all(bf16x8 (&out)[TN]) const {
+    static_for<0, TN>([&](auto jc) { decode<S, decltype(jc)::value>(out[decltype(jc)::value]); });
+  }
+};
+
+// Tile coordinates of workgroup `bid` out of `nb`: XCD-contiguous, then grouped by kGroupM rows.
 __device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
   int id = bid;
   if ((nb & 7) == 0) id = (bid & 7) * (nb >> 3) + (bid >> 3);
@@ -257,85 +354,84 @@ __device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_
   tn = in_g / gsize;
 }
 
-template <int TM, int TN>
-struct Frags {
-  bf16x8 a[2][TM], b[2][TN];
-};
-
-template <int TM, int TN, int BUF>
-__device__ __forceinline__ void read_frags(const uint8_t* stage, uint32_t a_base, uint32_t b_base,
-                                           uint32_t coff, Frags<TM, TN>& f) {
+template <int TM>
+__device__ __forceinline__ void read_a(const uint8_t* stage, uint32_t a_base, uint32_t coff,
+                                       bf16x8 (&f)[TM]) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
-    f.a[BUF][i] = *reinterpret_cast<const bf16x8*>(stage + a_base + i * 32 * kRowBytes + coff);
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-    f.b[BUF][j] = *reinterpret_cast<const bf16x8*>(stage + b_base + j * 32 * kRowBytes + coff);
+    f[i] = *reinterpret_cast<const bf16x8*>(stage + a_base + i * 32 * kRowBytes + coff);
 }
 
-// One K step on LDS stage `cur`: four 16-wide sub-steps.  FRAG_DB: each sub-step reads the next
-// sub-step's fragments ahead of its own MFMAs.  When STORE, sub-step ks also decodes part ks of
-// the next step's codes into `nxt` and, at its end (LOAD), reloads the finished pieces for step
-// kt_load.
-// Scheduling groups ask for every MFMA to be followed by a slice of the sub-step's other work, so
-// the matrix pipe keeps issuing while the VALU decodes and the LDS reads and writes proceed; a
-// scheduling fence closes each sub-step so later fragments are not hoisted (and kept live) early.
-template <bool STORE, bool LOAD, bool FRAG_DB, int TM, int TN, class SA, class SB>
+// One K step on LDS stage `cur`, as four sub-steps of TM x TN MFMAs.  MORE: stage the next step
+// into `nxt` during sub-steps 0..2, then (after a barrier) read its first operands during
+// sub-step 3; RELOAD: reload the staged pieces for step kt_load.  On entry fa[0] / fb[0] hold
+// sub-step 0's operands; on exit (MORE) they hold the next step's.
+// The other work of a sub-step is cut into tasks (an A fragment read, a raw B read, a B tile
+// decode, one staged chunk) that are spread evenly over the slots after its MFMAs; each slot is
+// fenced from the scheduler so the matrix pipe gets an MFMA between every few other instructions.
+template <bool MORE, bool RELOAD, int TM, int TN, class SA, class SB, class BR>
 __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_t a_base,
-                                       uint32_t b_base, const uint32_t (&coff)[4], SA& sa, SB& sb,
+                                       const uint32_t (&coff)[4], SA& sa, SB& sb, BR& br,
+                                       bf16x8 (&fa)[2][TM], bf16x8 (&fb)[2][TN],
                                        v16f (&acc)[TM][TN], int kt_load, bool partial_load) {
-  Frags<TM, TN> f;
-  if constexpr (FRAG_DB) read_frags<TM, TN, 0>(cur, a_base, b_base, coff[0], f);
-  static_for<0, 4>([&](auto ksc) {
-    constexpr int ks = decltype(ksc)::value;
-    constexpr int buf = FRAG_DB ? (ks & 1) : 0;
-    if constexpr (FRAG_DB) {
-      if constexpr (ks < 3) read_frags<TM, TN, (ks + 1) & 1>(cur, a_base, b_base, coff[ks + 1], f);
-    } else {
-      read_frags<TM, TN, 0>(cur, a_base, b_base, coff[ks], f);
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[buf][i], f.b[buf][j],
-                                                            acc[i][j], 0, 0, 0);
-    if constexpr (STORE) {
-      sa.template store_part<ks>(nxt);
-      sb.template store_part<ks>(nxt);
-    }
-    // Interleave: each MFMA is followed by a slice of the sub-step's other instructions.
+  static_for<0, 4>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    constexpr int nb = (s + 1) & 1;                                      // operand buffer filled
+    constexpr bool last = s == 3;
+    constexpr int kRaw = (last && MORE) ? TN * BR::kQ : 0;               // raw B reads of nxt
+    constexpr int kRd = (!last || MORE) ? TM : 0;                         // A fragment reads
+    constexpr int kDec = (!last || MORE) ? TN : 0;                        // B tile decodes
+    constexpr int kA = (!last && MORE) ? SA::template chunks_in_part<s>() : 0;
+    constexpr int kB = (!last && MORE) ? SB::template chunks_in_part<s>() : 0;
+    constexpr int kTasks = kRaw + kRd + kDec + kA + kB;
     constexpr int kM = TM * TN;
-    constexpr int kReads = FRAG_DB ? (ks < 3 ? TM + TN : 0) : 0;
-    constexpr int kChunksHere = STORE ? SA::template chunks_in_part<ks>() + SB::template chunks_in_part<ks>() : 0;
-    constexpr int kCvt = 4 * kChunksHere;
+    if constexpr (last && MORE) {
+      // Every write to `nxt` and every read of `cur` is complete in every wavefront past here.
+      __syncthreads();
+      br.take_scales();
+    }
+    auto task = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      if constexpr (t < kRaw) {
+        br.template read_raw<t / BR::kQ, t % BR::kQ>(nxt);
+      } else if constexpr (t < kRaw + kRd) {
+        constexpr int i = t - kRaw;
+        const uint8_t* stage = last ? nxt : cur;
+        fa[nb][i] = *reinterpret_cast<const bf16x8*>(stage + a_base + i * 32 * kRowBytes +
+                                                     coff[(s + 1) & 3]);
+      } else if constexpr (t < kRaw + kRd + kDec) {
+        constexpr int j = t - kRaw - kRd;
+        br.template decode<(s + 1) & 3, j>(fb[nb][j]);
+      } else if constexpr (t < kRaw + kRd + kDec + kA) {
+        sa.template store_chunk<SA::template nth_chunk<s, t - kRaw - kRd - kDec>()>(nxt);
+      } else {
+        sb.template store_chunk<SB::template nth_chunk<s, t - kRaw - kRd - kDec - kA>()>(nxt);
+      }
+    };
     static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-      constexpr int r0 = m * kReads / kM, r1 = (m + 1) * kReads / kM;
-      if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);   // DS read
-      constexpr int v0 = m * kCvt / kM, v1 = (m + 1) * kCvt / kM;
-      if constexpr (v1 > v0) __builtin_amdgcn_sched_group_barrier(0x002, v1 - v0, 0);   // VALU
-      constexpr int w0 = m * kChunksHere / kM, w1 = (m + 1) * kChunksHere / kM;
-      if constexpr (w1 > w0) __builtin_amdgcn_sched_group_barrier(0x200, w1 - w0, 0);   // DS write
+      constexpr int i = m / TN, j = m % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j],
+                                                          0, 0, 0);
+      static_for<m * kTasks / kM, (m + 1) * kTasks / kM>(task);
+      __builtin_amdgcn_sched_barrier(0);
     });
-    // Close the scheduling region: later sub-steps' reads must not be hoisted into this one.
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (STORE && LOAD) {
-      sa.template load_part<ks>(kt_load, partial_load);
-      sb.template load_part<ks>(kt_load, partial_load);
+    if constexpr (RELOAD && !last) {
+      sa.template load_part<s>(kt_load, partial_load);
+      sb.template load_part<s>(kt_load, partial_load);
     }
   });
 }
 
-template <int AF, int BF, bool BIAS, int BM, int BN, int WM, int WN, bool FRAG_DB>
+template <int AF, int BF, bool BIAS, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;     // WM x WN wavefronts
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  constexpr int kStageBytes = (BM + BN) * kRowBytes;
-  static_assert(BM * BN * 2 <= 2 * kStageBytes, "the bf16 output tile must fit the operand stages");
+  constexpr int kBPitch = BF == kFp8 ? 64 : 32;
+  constexpr int kBRegion = BM * kRowBytes;
+  constexpr int kStageBytes = kBRegion + BN * kBPitch;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -349,55 +445,67 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   const int64_t bz = blockIdx.y;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  Stager<AF, BM, NT, 0> sa;
-  Stager<BF, BN, NT, 1> sb;
+  constexpr int kPerA = Stager<AF, BM, NT, true, 0, 1>::kPer;
+  constexpr int kPerB = Stager<BF, BN, NT, false, 0, 1>::kPer;
+  constexpr int kNA = kPerA < 2 ? kPerA : 2;
+  constexpr int kNB = kPerB < 2 ? kPerB : 2;
+  Stager<AF, BM, NT, true, 0, kNA> sa;
+  Stager<BF, BN, NT, false, kParts - kNB, kNB> sb;
   sa.init(p.a + bz * p.stride_a, p.a_s + bz * p.stride_as, m0, p.M, p.K, false, 0);
-  sb.init(p.b + bz * p.stride_b, p.b_s + bz * p.stride_bs, n0, p.N, p.K, BF == kFp8, BM);
+  sb.init(p.b + bz * p.stride_b, nullptr, n0, p.N, p.K, BF == kFp8, kBRegion);
+  BRegs<BF, TN> br;
+  br.init(p.b_s + bz * p.stride_bs, n0 + wn * WTN, p.N, p.K, kBRegion, wn * WTN);
 
-  // Operand fragment offsets: rows wm*WTM + 32i + l32 (A) and BM + wn*WTN + 32j + l32 (B) share
-  // swz(l32), so four chunk offsets (one per 16-wide K sub-step) serve every fragment.
+  // A fragment rows wm*WTM + 32i + l32 share swz(l32), so four chunk offsets (one per sub-step,
+  // chunk 4h + s: K [32h + 8s, 32h + 8s + 8)) serve every fragment.
   const uint32_t a_base = static_cast<uint32_t>((wm * WTM + l32) * kRowBytes);
-  const uint32_t b_base = static_cast<uint32_t>((BM + wn * WTN + l32) * kRowBytes);
   uint32_t coff[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) coff[ks] = static_cast<uint32_t>(((2 * ks + h) ^ swz(l32)) << 4);
+  for (int ks = 0; ks < 4; ++ks) coff[ks] = static_cast<uint32_t>(((4 * h + ks) ^ swz(l32)) << 4);
 
   v16f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+  bf16x8 fa[2][TM], fb[2][TN];
 
-  // Pipeline: step k's codes are decoded into LDS stage k & 1 during step k-1's MFMAs, piece by
-  // piece, and each piece is reloaded for step k+1 right after its decode.
+  // Pipeline: step k's codes are staged into LDS stage k & 1 during step k-1, piece by piece, and
+  // each piece is reloaded for step k+1 right after it is staged.
   const int KT = (p.K + kBK - 1) / kBK;
   const int last_partial = (p.K % kBK) != 0 ? KT - 1 : -1;
   sa.load_all(0, last_partial == 0);
   sb.load_all(0, last_partial == 0);
+  br.load_scales(0);
   sa.store_all(lds);
   sb.store_all(lds);
   if (KT > 1) {
-    static_for<0, 4>([&](auto pc) {
+    static_for<0, kParts>([&](auto pc) {
       constexpr int P = decltype(pc)::value;
       sa.template load_part<P>(1, last_partial == 1);
       sb.template load_part<P>(1, last_partial == 1);
     });
   }
   __syncthreads();
+  br.take_scales();
+  read_a<TM>(lds, a_base, coff[0], fa[0]);
+  br.read_raw_all(lds);
+  br.template decode_all<0>(fb[0]);
+  if (KT > 1) br.load_scales(1);
+
   int kt = 0;
   for (; kt + 2 < KT; ++kt) {
-    k_step<true, true, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes,
-                                a_base, b_base, coff, sa, sb, acc, kt + 2, kt + 2 == last_partial);
-    __syncthreads();
+    k_step<true, true>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes, a_base,
+                       coff, sa, sb, br, fa, fb, acc, kt + 2, kt + 2 == last_partial);
+    br.load_scales(kt + 2);
   }
   if (kt + 1 < KT) {
-    k_step<true, false, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes,
-                                 a_base, b_base, coff, sa, sb, acc, 0, false);
-    __syncthreads();
+    k_step<true, false>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes, a_base,
+                        coff, sa, sb, br, fa, fb, acc, 0, false);
     ++kt;
   }
-  k_step<false, false, FRAG_DB>(lds + (kt & 1) * kStageBytes, lds, a_base, b_base, coff, sa, sb,
-                                acc, 0, false);
+  k_step<false, false>(lds + (kt & 1) * kStageBytes, lds, a_base, coff, sa, sb, br, fa, fb, acc,
+                       0, false);
 
   // Epilogue, staged through LDS: fp32 + bias, one bf16 rounding, written into a row-major bf16
   // tile [BM][BN] (16-byte chunk c of row r at chunk c ^ (4 * bit 2 of r): the two row groups a
@@ -449,22 +557,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
 }
 
-template <int AF, int BF, int BM, int BN, int WM, int WN, bool FRAG_DB>
+template <int AF, int BF, int BM, int BN>
+constexpr int lds_bytes() {
+  constexpr int stages = 2 * (BM * kRowBytes + BN * (BF == kFp8 ? 64 : 32));
+  constexpr int tile = BM * BN * 2;
+  return stages > tile ? stages : tile;
+}
+
+template <int AF, int BF, int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c};
-  constexpr int kLds = 2 * (BM + BN) * kRowBytes;
+  constexpr int kLds = lds_bytes<AF, BF, BM, BN>();
+  static_assert(kLds <= 160 * 1024, "LDS");
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
-  auto k = g.bias ? gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN, FRAG_DB>
-                  : gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN, FRAG_DB>;
+  auto k = g.bias ? gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN>
+                  : gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN>;
   // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
   static const hipError_t attr_ok = [] {
     hipError_t e1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN, FRAG_DB>),
+        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     hipError_t e2 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN, FRAG_DB>),
+        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     return e1 != hipSuccess ? e1 : e2;
   }();
@@ -483,9 +599,9 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   // A last partial wave of 256x256 tiles is not worth splitting further: on 4096x7168 (448 tiles,
   // 1.75 waves) the 192 tiles of the second wave run 18% faster per CU than a full wave does, and
   // finishing them as 256 tiles of 256x192 in a second launch measured the same total time.
-  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 4, 2, true>(g, stream);
-  if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2, true>(g, stream);
-  return launch_tile<AF, BF, 64, 64, 2, 2, false>(g, stream);
+  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 2, 4>(g, stream);
+  if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, stream);
+  return launch_tile<AF, BF, 64, 64, 2, 2>(g, stream);
 }
 
 }  // namespace
