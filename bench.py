@@ -34,8 +34,10 @@ METRIC = "block-scaled GEMM TFLOP/s (% MFMA peak) + act_quant GB/s (% HBM peak)"
 ACT_QUANT_BYTES_PER_ELEM = 2 + 1 + 1 / 32      # bf16 in, E4M3 code out, one scale byte per 32
 
 
-GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip"]
-ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip"]
+GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip",
+                "block_scaled_precision_act_amd/csrc/mx_quant.h"]
+ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip",
+                     "block_scaled_precision_act_amd/csrc/mx_quant.h"]
 COPY_BYTES = 1 << 30          # the plain copy used to calibrate the HBM byte counters
 COPY_REPS = 3                 # ... run this many times, last in the program
 
@@ -175,6 +177,32 @@ def main():
                           "bf16 MFMA)", "avg_launch_ms": round(gemm_ms, 5),
                 "algorithmic_flops_per_launch": flops}
 
+    # ---- the same GEMM emitting the next layer's activation operand (E4M3 codes + per-32 E8M0
+    # bytes of the bf16 output): the quantizing epilogue against the bf16 output followed by
+    # act_quant on it, on the step's inputs.
+    qn = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    qsn = torch.empty((M, N // 32), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        mx.mx_gemm_fp8_fp4_quant(q, s, b, b_s, qn, qsn, bias=bias, stream=stream)
+
+    def unfused():
+        mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
+        mx.mx_act_quant(c, qn, qsn, stream=stream)
+
+    for _ in range(5):
+        fused()
+        unfused()
+    fused_ms = time_events(fused, 50, torch)
+    unfused_ms = time_events(unfused, 50, torch)
+    next_layer = {"workload": "FP8xMXFP4 GEMM 4096x7168x2048 + bias -> E4M3 [4096, 7168] + "
+                              "E8M0 [4096, 224] for the next layer",
+                  "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
+                  "fused_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                  "speedup": round(unfused_ms / fused_ms, 3),
+                  "fused_traffic": _traffic("gemm_fp8_fp4_quant_4096x7168x2048", GEMM_SOURCES)}
+    del qn, qsn
+
     # ---- standalone act_quant on [16384, 7168], sustained: back-to-back launches rotating over
     # three input/output sets (1.07 GB, far beyond the 256 MB last-level cache), so each launch
     # reads its input from HBM and pays for the previous launch's write-back.
@@ -227,6 +255,7 @@ def main():
                       "weight_scales": "E8M0 118..136", "parallelism": "single GPU"},
            "roofline": roofline, "act_quant": act_quant,
            "gemm_only_tflops": round(gemm_tflops, 2)}
+    out["next_layer_quant"] = next_layer
     if others is not None:
         out["other_configs"] = others
     if not args.no_cpu:
@@ -325,11 +354,17 @@ def summarize(stats_dir, fetch_dir, write_dir):
     aq_grids = [g for (k, g, _) in list(fetch) + list(write) if "act_quant_kernel" in k]
     aq_grid = max(aq_grids) if aq_grids else None
     aq_alg = ACT_QUANT_BYTES_PER_ELEM * 16384 * 7168
-    gemm_alg = 4096 * 2048 + 4096 * 64 + 7168 * 1024 + 7168 * 64 + 2 * 7168 + 2 * 4096 * 7168
+    gemm_in = 4096 * 2048 + 4096 * 64 + 7168 * 1024 + 7168 * 64 + 2 * 7168
+    gemm_alg = gemm_in + 2 * 4096 * 7168
+    gemm_q_alg = gemm_in + 4096 * 7168 + 4096 * 7168 // 32
     out = {}
+    # template arguments <A format, B format, bias, quantized output, ...> pick the variant
     for name, part, grid, files, alg in (
             ("act_quant_16384x7168", "act_quant_kernel", aq_grid, ACT_QUANT_SOURCES, aq_alg),
-            ("gemm_fp8_fp4_4096x7168x2048", "gemm_bf16_kernel", None, GEMM_SOURCES, gemm_alg)):
+            ("gemm_fp8_fp4_4096x7168x2048", "gemm_bf16_kernel<0, 4, true, false,", None,
+             GEMM_SOURCES, gemm_alg),
+            ("gemm_fp8_fp4_quant_4096x7168x2048", "gemm_bf16_kernel<0, 4, true, true,", None,
+             GEMM_SOURCES, gemm_q_alg)):
         f, w = pick(fetch, part, grid), pick(write, part, grid)
         if f is None or w is None or not f_factor or not w_factor:
             continue

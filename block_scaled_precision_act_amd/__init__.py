@@ -45,6 +45,10 @@ for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
                                               _I, _I, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_bias_strided_batched"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                                    _I, _I, _I, _I, _I, _I, _P]
+for _n in ("fp8_fp4", "fp8_fp8"):
+    _SIGS[f"mx_gemm_{_n}_quant"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_quant_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                                    _I, _I, _I, _I, _I, _I, _I, _P]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -156,3 +160,33 @@ def mx_gemm_fp8_fp8(a, a_s, b, b_s, c, bias=None, stream=None):
 def mx_gemm_fp4_fp4(a, a_s, b, b_s, c, bias=None, stream=None):
     """As mx_gemm_fp8_fp4 with a: packed E2M1 [(B,) M, K/2]."""
     _gemm("fp4_fp4", a, a_s, b, b_s, c, bias, K=2 * a.shape[-1], stream=stream)
+
+
+def _gemm_quant(kind: str, a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    M, N, K = q.shape[-2], q.shape[-1], a.shape[-1]
+    lib = load()
+    st = _stream(stream)
+    if q.dim() == 2:
+        name = f"mx_gemm_{kind}_quant"
+        r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), _ptr(q),
+                               _ptr(q_s), M, N, K, st)
+    else:
+        B = q.shape[0]
+        strides = [t.stride(0) if t.dim() == 3 else 0 for t in (a, a_s, b, b_s)]
+        sbias = bias.stride(0) if (bias is not None and bias.dim() == 2) else 0
+        name = f"mx_gemm_{kind}_quant_strided_batched"
+        r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), _ptr(q),
+                               _ptr(q_s), M, N, K, B, *strides, sbias, q.stride(0),
+                               q_s.stride(0), st)
+    _check(name, r)
+
+
+def mx_gemm_fp8_fp4_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4, but the bf16 output is written as the next layer's activation operand:
+    q: E4M3 [(B,) M, N] and q_s: E8M0 [(B,) M, N/32] (N % 32 == 0)."""
+    _gemm_quant("fp8_fp4", a, a_s, b, b_s, q, q_s, bias, stream)
+
+
+def mx_gemm_fp8_fp8_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_quant with b: E4M3 [(B,) N, K] and b_s: [(B,) ceil(N/32), K/32]."""
+    _gemm_quant("fp8_fp8", a, a_s, b, b_s, q, q_s, bias, stream)

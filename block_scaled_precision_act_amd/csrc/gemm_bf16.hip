@@ -32,8 +32,11 @@
 //   * the workgroup -> tile map keeps consecutive tiles on one XCD (workgroups are dealt to the 8
 //     XCDs round-robin) and walks them in groups of kGroupM tile rows, so an XCD's L2 holds the
 //     A rows and B rows its running tiles share;
-//   * epilogue: fp32 + bias, one RNE rounding, staged through LDS for 16-byte row stores.
+//   * epilogue: fp32 + bias, one RNE rounding, staged through LDS for 16-byte row stores; or, for
+//     the quantizing entry points, the same bf16 tile quantized per 32 columns to E4M3 + E8M0
+//     (the next layer's activation operand) without writing the bf16 values out.
 #include "mx_internal.h"
+#include "mx_quant.h"
 
 namespace mx {
 namespace {
@@ -69,6 +72,9 @@ struct Args {
   int M, N, K;
   int tiles_m, tiles_n;
   int64_t stride_a, stride_as, stride_b, stride_bs, stride_bias, stride_c;
+  uint8_t* q;
+  uint8_t* qs;
+  int64_t stride_q, stride_qs;
 };
 
 // fp32 value of an E8M0 byte (2^(b-127)); byte 0 is the fp32 subnormal 2^-127.
@@ -423,7 +429,9 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
   });
 }
 
-template <int AF, int BF, bool BIAS, int BM, int BN, int WM, int WN>
+// QUANT: instead of the bf16 output, write its per-32 E4M3 codes and E8M0 bytes (the next
+// layer's activation operand), computed from the same bf16 values with the act_quant arithmetic.
+template <int AF, int BF, bool BIAS, bool QUANT, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;     // WM x WN wavefronts
@@ -537,21 +545,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
   __syncthreads();
   constexpr int kChunksPerRow = BN / 8;
-  uint16_t* c = p.c + bz * p.stride_c;
-  for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-    const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-    const int row = m0 + trow, col = n0 + tch * 8;
-    if (row >= p.M || col >= p.N) continue;
-    const int ch = tch ^ (((trow >> 2) & 1) << 2);
-    const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
-    uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
-    if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
+  if constexpr (QUANT) {
+    // Four consecutive lanes hold the four 16-byte chunks of one 32-column block of a row
+    // (kChunksPerRow % 4 == 0), and every lane of the workgroup runs every iteration (the tile's
+    // chunk count is a multiple of the workgroup size), so the quad permutes only mix live lanes.
+    // N % 32 == 0: a block is entirely inside or entirely outside the matrix.
+    static_assert(kChunksPerRow % 4 == 0 && (BM * kChunksPerRow) % NT == 0, "quad blocks");
+    uint8_t* q = p.q + bz * p.stride_q;
+    uint8_t* qs = p.qs + bz * p.stride_qs;
+    const int nb = p.N / 32;
+    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+      const int row = m0 + trow, col = n0 + tch * 8;
+      const int ch = tch ^ (((trow >> 2) & 1) << 2);
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
+      const QuantChunk qc = quant_chunk(v);
+      if (row < p.M && col < p.N) {
+        *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row) * p.N + col) = qc.codes;
+        if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
+      }
+    }
+  } else {
+    uint16_t* c = p.c + bz * p.stride_c;
+    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+      const int row = m0 + trow, col = n0 + tch * 8;
+      if (row >= p.M || col >= p.N) continue;
+      const int ch = tch ^ (((trow >> 2) & 1) << 2);
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
+      uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
+      if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
-        if (col + k < p.N) dst[k] = static_cast<uint16_t>((k & 1) ? w >> 16 : w);
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
+          if (col + k < p.N) dst[k] = static_cast<uint16_t>((k & 1) ? w >> 16 : w);
+        }
       }
     }
   }
@@ -564,29 +594,34 @@ constexpr int lds_bytes() {
   return stages > tile ? stages : tile;
 }
 
+template <int AF, int BF, bool BIAS, bool QUANT, int BM, int BN, int WM, int WN>
+hipError_t launch_kernel(const Args& p, dim3 grid, hipStream_t stream) {
+  constexpr int kLds = lds_bytes<AF, BF, BM, BN>();
+  static_assert(kLds <= 160 * 1024, "LDS");
+  auto k = gemm_bf16_kernel<AF, BF, BIAS, QUANT, BM, BN, WM, WN>;
+  // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
+  static const hipError_t attr_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (attr_ok != hipSuccess) return attr_ok;
+  hipLaunchKernelGGL(k, grid, dim3(64 * WM * WN), kLds, stream, p);
+  return hipGetLastError();
+}
+
 template <int AF, int BF, int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
-         g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c};
-  constexpr int kLds = lds_bytes<AF, BF, BM, BN>();
-  static_assert(kLds <= 160 * 1024, "LDS");
+         g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
+         g.q, g.qs, g.stride_q, g.stride_qs};
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
-  auto k = g.bias ? gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN>
-                  : gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN>;
-  // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
-  static const hipError_t attr_ok = [] {
-    hipError_t e1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, true, BM, BN, WM, WN>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    hipError_t e2 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gemm_bf16_kernel<AF, BF, false, BM, BN, WM, WN>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    return e1 != hipSuccess ? e1 : e2;
-  }();
-  if (attr_ok != hipSuccess) return attr_ok;
-  hipLaunchKernelGGL(k, grid, dim3(64 * WM * WN), kLds, stream, p);
-  return hipGetLastError();
+  if constexpr (AF == kFp8) {
+    if (g.q) {
+      return g.bias ? launch_kernel<AF, BF, true, true, BM, BN, WM, WN>(p, grid, stream)
+                    : launch_kernel<AF, BF, false, true, BM, BN, WM, WN>(p, grid, stream);
+    }
+  }
+  return g.bias ? launch_kernel<AF, BF, true, false, BM, BN, WM, WN>(p, grid, stream)
+                : launch_kernel<AF, BF, false, false, BM, BN, WM, WN>(p, grid, stream);
 }
 
 template <int AF, int BF>

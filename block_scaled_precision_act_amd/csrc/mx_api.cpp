@@ -108,6 +108,11 @@ struct GemmCall {
   int64_t M, N, K, batch;
   int64_t sa, sas, sb, sbs, sbias, sc;
   bool needs_bias;
+  // Quantized output (instead of c): E4M3 codes [M, N] and E8M0 bytes [M, N/32].
+  bool quant = false;
+  void* q = nullptr;
+  void* qs = nullptr;
+  int64_t sq = 0, sqs = 0;
 };
 
 int validate_gemm(const GemmCall& g) {
@@ -116,14 +121,18 @@ int validate_gemm(const GemmCall& g) {
   if (g.M > 0 && g.M > mx::kMaxMatrixElems / g.K) return MX_ERR_SHAPE;
   if (g.N > 0 && g.N > mx::kMaxMatrixElems / g.K) return MX_ERR_SHAPE;
   if (g.M > 0 && g.N > 0 && g.M > mx::kMaxMatrixElems / g.N) return MX_ERR_SHAPE;
-  if (g.sa < 0 || g.sas < 0 || g.sb < 0 || g.sbs < 0 || g.sbias < 0 || g.sc < 0)
+  if (g.quant && g.N % 32 != 0) return MX_ERR_SHAPE;
+  if (g.sa < 0 || g.sas < 0 || g.sb < 0 || g.sbs < 0 || g.sbias < 0 || g.sc < 0 || g.sq < 0 ||
+      g.sqs < 0)
     return MX_ERR_STRIDE;
-  if (g.batch > 1 && g.sc == 0) return MX_ERR_STRIDE;
+  if (g.batch > 1 && (g.quant ? (g.sq == 0 || g.sqs == 0) : g.sc == 0)) return MX_ERR_STRIDE;
   if (g.M == 0 || g.N == 0 || g.batch == 0) return MX_OK;
-  if (!g.a || !g.a_s || !g.b || !g.b_s || !g.c) return MX_ERR_NULL;
+  if (!g.a || !g.a_s || !g.b || !g.b_s) return MX_ERR_NULL;
+  if (g.quant ? (!g.q || !g.qs) : !g.c) return MX_ERR_NULL;
   if (g.needs_bias && !g.bias) return MX_ERR_NULL;
   if (!mx::aligned16(g.a) || !mx::aligned16(g.b)) return MX_ERR_ALIGN;
   if (g.sa % 16 != 0 || g.sb % 16 != 0) return MX_ERR_ALIGN;
+  if (g.quant && (!mx::aligned16(g.q) || g.sq % 16 != 0)) return MX_ERR_ALIGN;
   return MX_OK;
 }
 
@@ -149,6 +158,13 @@ int gemm_impl(const GemmCall& g, void* stream) {
   p.stride_bs = g.sbs;
   p.stride_bias = g.sbias;
   p.stride_c = g.sc;
+  if (g.quant) {
+    p.c = nullptr;
+    p.q = static_cast<uint8_t*>(g.q);
+    p.qs = static_cast<uint8_t*>(g.qs);
+    p.stride_q = g.sq;
+    p.stride_qs = g.sqs;
+  }
   hipError_t e = mx::launch_gemm(g.a_fmt, g.b_fmt, p, dev, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
@@ -164,6 +180,20 @@ GemmCall batched(int af, int bf, const void* a, const void* a_s, const void* b, 
                  bool needs_bias) {
   return GemmCall{af, bf, a, a_s, b, b_s, bias, c, M, N, K, batch,
                   sa, sas, sb, sbs, sbias, sc, needs_bias};
+}
+
+GemmCall quantized(int af, int bf, const void* a, const void* a_s, const void* b,
+                   const void* b_s, const void* bias, void* q, void* qs, int64_t M, int64_t N,
+                   int64_t K, int64_t batch, int64_t sa, int64_t sas, int64_t sb, int64_t sbs,
+                   int64_t sbias, int64_t sq, int64_t sqs) {
+  GemmCall g{af, bf, a, a_s, b, b_s, bias, nullptr, M, N, K, batch,
+             sa, sas, sb, sbs, sbias, 0, false};
+  g.quant = true;
+  g.q = q;
+  g.qs = qs;
+  g.sq = sq;
+  g.sqs = sqs;
+  return g;
 }
 
 }  // namespace
@@ -253,5 +283,28 @@ MX_GEMM_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
 MX_GEMM_ENTRY_POINTS(fp4_fp4, mx::kFp4, mx::kFp4)
 
 #undef MX_GEMM_ENTRY_POINTS
+
+#define MX_GEMM_QUANT_ENTRY_POINTS(NAME, AF, BF)                                              \
+  int mx_gemm_##NAME##_quant(const void* a, const void* a_s, const void* b, const void* b_s,  \
+                             const void* bias, void* q, void* q_s, int64_t M, int64_t N,      \
+                             int64_t K, void* stream) {                                       \
+    return gemm_impl(quantized(AF, BF, a, a_s, b, b_s, bias, q, q_s, M, N, K, 1, 0, 0, 0, 0,  \
+                               0, 0, 0),                                                      \
+                     stream);                                                                 \
+  }                                                                                           \
+  int mx_gemm_##NAME##_quant_strided_batched(                                                 \
+      const void* a, const void* a_s, const void* b, const void* b_s, const void* bias,       \
+      void* q, void* q_s, int64_t M, int64_t N, int64_t K, int64_t batch, int64_t sa,         \
+      int64_t sas, int64_t sb, int64_t sbs, int64_t sbias, int64_t sq, int64_t sqs,           \
+      void* stream) {                                                                         \
+    return gemm_impl(quantized(AF, BF, a, a_s, b, b_s, bias, q, q_s, M, N, K, batch, sa, sas, \
+                               sb, sbs, sbias, sq, sqs),                                      \
+                     stream);                                                                 \
+  }
+
+MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp4, mx::kFp8, mx::kFp4)
+MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
+
+#undef MX_GEMM_QUANT_ENTRY_POINTS
 
 }  // extern "C"

@@ -17,9 +17,12 @@ struct GemmProblem {
   const uint8_t* b;
   const uint8_t* b_s;
   const uint16_t* bias;   // nullptr: no bias
-  uint16_t* c;
+  uint16_t* c;            // bf16 output, or nullptr when the output is quantized (q, qs)
   int M, N, K, batch;
   int64_t stride_a, stride_as, stride_b, stride_bs, stride_bias, stride_c;
+  uint8_t* q = nullptr;   // E4M3 codes of the bf16 output [M, N] (N % 32 == 0)
+  uint8_t* qs = nullptr;  // their E8M0 bytes [M, N/32]
+  int64_t stride_q = 0, stride_qs = 0;
 };
 
 struct DeviceInfo {

@@ -1,0 +1,73 @@
+// Per-32 E4M3 + E8M0 quantization of bf16 values held in registers, for gfx950 kernels: the one
+// implementation act_quant and the quantizing GEMM epilogue share, so both produce the same bytes
+// for the same bf16 input.
+//
+// Semantics ("formats.py" page: act_scale, _log2_ceil_pow2, act_quant), per 32 consecutive
+// elements of a row:
+//   amax = max(max |x|, fp32(1e-4)); t = fp32(amax * fp32(1/448));
+//   E = exponent field of t - 127, plus one when t's mantissa is non-zero; byte = E + 127;
+//   q = e4m3_rne(clamp(x * 2^-E, -448, 448)).
+// x * 2^-E is exact (a power-of-two scaling that cannot overflow, and an underflowing product
+// rounds to a signed zero, as the exact value does), and v_cvt_pk_fp8_f32 rounds to nearest even
+// into OCP e4m3fn with subnormals and signed zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mx {
+
+constexpr uint32_t kInv448Bits = 0x3B124925u;   // fp32(1/448)
+
+// quad_perm [1,0,3,2] then [2,3,0,1]: every lane of a DPP quad ends with the quad's max.  All
+// four lanes of the quad must be active.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+
+// Largest |bf16| bit pattern of 8 packed bf16: |bf16| patterns compare as unsigned integers
+// exactly like the values they encode.
+__device__ __forceinline__ uint32_t abs_max_bits(uint4 w) {
+  uint32_t m01 = max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu);
+  uint32_t m23 = max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu);
+  uint32_t m45 = max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu);
+  uint32_t m67 = max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu);
+  return max(max(m01, m23), max(m45, m67));
+}
+
+__device__ __forceinline__ float clamp448(float y) {
+  return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f);
+}
+
+// Four bf16 (two packed pairs) times inv_s -> four E4M3 codes in one dword (element order kept).
+__device__ __forceinline__ uint32_t encode4(uint32_t lo_pair, uint32_t hi_pair, float inv_s) {
+  float y0 = clamp448(__uint_as_float(lo_pair << 16) * inv_s);
+  float y1 = clamp448(__uint_as_float(lo_pair & 0xFFFF0000u) * inv_s);
+  float y2 = clamp448(__uint_as_float(hi_pair << 16) * inv_s);
+  float y3 = clamp448(__uint_as_float(hi_pair & 0xFFFF0000u) * inv_s);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, r, true);
+  return static_cast<uint32_t>(r);
+}
+
+struct QuantChunk {
+  uint2 codes;      // E4M3 codes of the lane's 8 values
+  uint32_t byte;    // E8M0 byte of the 32-block (E + 127, in [105, 247])
+};
+
+// The lane holds 8 consecutive bf16 of a row; the four lanes of its DPP quad hold one 32-block.
+__device__ __forceinline__ QuantChunk quant_chunk(uint4 w) {
+  const uint32_t amax_bits = quad_max(abs_max_bits(w));
+  const float amax = fmaxf(__uint_as_float(amax_bits << 16), 1e-4f);
+  const uint32_t t = __float_as_uint(amax * __uint_as_float(kInv448Bits));
+  QuantChunk r;
+  r.byte = (t >> 23) + ((t & 0x7FFFFFu) != 0u);
+  const float inv_s = __uint_as_float((254u - r.byte) << 23);     // 2^-E, a normal fp32
+  r.codes.x = encode4(w.x, w.y, inv_s);
+  r.codes.y = encode4(w.z, w.w, inv_s);
+  return r;
+}
+
+}  // namespace mx

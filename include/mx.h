@@ -163,6 +163,46 @@ int mx_gemm_fp4_fp4_bias_strided_batched(const void* a, const void* a_scale, con
                                          int64_t stride_b, int64_t stride_b_scale,
                                          int64_t stride_bias, int64_t stride_c, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * GEMM with a quantized output: the next layer's activation operand instead of bf16.
+ *
+ * The "fp4-gemm README" page lists an epilogue that emits the following projection's quantized
+ * input directly, so that no bf16 tensor is materialized and no separate quantization launch is
+ * needed (API list and the paragraph after the schedule variants); the "AstrAI commit log" page
+ * has an FP8-in / FP8-out GEMM op.  Here the output format is this library's activation format:
+ *   y[m,n]  = bf16_rne( sum_k A[m,k] B[n,k] + bias[n] )     exactly the value the bf16 entry
+ *                                                           points above write for the same call;
+ *   (q, q_scale) = act_quant(y)                             per 32 consecutive n of each row,
+ *                                                           exactly as mx_act_quant does.
+ * The result is byte-identical to mx_gemm_* followed by mx_act_quant on the bf16 output.
+ *   bias     bf16 [N], or NULL for no bias
+ *   q        E4M3 codes [M, N] (16-byte aligned; written)
+ *   q_scale  E8M0 bytes [M, N/32] (written)
+ * N must be a multiple of 32 (MX_ERR_SHAPE otherwise).  Operands, formats and the other rules as
+ * for mx_gemm_fp8_fp4 / mx_gemm_fp8_fp8.  Batched: q + i*stride_q, q_scale + i*stride_q_scale
+ * (bytes; stride_q a multiple of 16; neither 0 when batch > 1).
+ * ------------------------------------------------------------------------------------------- */
+int mx_gemm_fp8_fp4_quant(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                          const void* bias, void* q, void* q_scale, int64_t M, int64_t N,
+                          int64_t K, void* stream);
+int mx_gemm_fp8_fp4_quant_strided_batched(const void* a, const void* a_scale, const void* b,
+                                          const void* b_scale, const void* bias, void* q,
+                                          void* q_scale, int64_t M, int64_t N, int64_t K,
+                                          int64_t batch, int64_t stride_a, int64_t stride_a_scale,
+                                          int64_t stride_b, int64_t stride_b_scale,
+                                          int64_t stride_bias, int64_t stride_q,
+                                          int64_t stride_q_scale, void* stream);
+int mx_gemm_fp8_fp8_quant(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                          const void* bias, void* q, void* q_scale, int64_t M, int64_t N,
+                          int64_t K, void* stream);
+int mx_gemm_fp8_fp8_quant_strided_batched(const void* a, const void* a_scale, const void* b,
+                                          const void* b_scale, const void* bias, void* q,
+                                          void* q_scale, int64_t M, int64_t N, int64_t K,
+                                          int64_t batch, int64_t stride_a, int64_t stride_a_scale,
+                                          int64_t stride_b, int64_t stride_b_scale,
+                                          int64_t stride_bias, int64_t stride_q,
+                                          int64_t stride_q_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,8 @@ Everything here is written to be read against the pages it follows, not to be fa
   (bf16 -> fp32 is exact from the raw bits).
 * "AstrAI commit log" page: the fused-bias commit (bias added in fp32 before the single bf16
   rounding of the GEMM output).
+* "fp4-gemm README" page: the epilogue that emits the next projection's quantized input (O4: the
+  bf16 GEMM output quantized with act_quant).
 
 Decoded values and the GEMM are carried in float64: every decoded value has at most 4
 significant bits times a power of two, so every product of two of them is exact in float64, and
@@ -29,7 +31,8 @@ Readings taken where the pages are silent (each is listed in the design notes as
 * Non-finite activations, NaN E4M3 codes (0x7F, 0xFF) and the NaN scale byte 255 are refused.
 
 No function here is "parity unpinned" except the GEMM below the stated tolerance (the bf16 output
-of any correct implementation may differ from another's inside that bound).
+of any correct implementation may differ from another's inside that bound); the quantized GEMM
+output inherits that freedom and is accepted by the bound quant_output_within derives.
 """
 from __future__ import annotations
 
@@ -308,3 +311,65 @@ def within_tolerance(out_bits, ref, S) -> np.ndarray:
     ok = np.abs(out - ref) <= np.ldexp(np.abs(ref), -7) + np.ldexp(S, -20)
     return ok & np.isfinite(out)
 
+
+
+# ----------------------------------------------------------------------------------------------
+# O4: the GEMM output quantized for the next layer (act_quant of the bf16 output)
+# ----------------------------------------------------------------------------------------------
+
+def f64_to_bf16_rne(x) -> np.ndarray:
+    """float64 -> raw bits (uint16) of the nearest bf16 value, ties to the even significand.
+
+    From the definition of the format: in the binade of |x| (exponent e = floor(log2|x|), and
+    e = -126 for the subnormal range) bf16 values are spaced 2^(e-7) apart; |x| is rounded to the
+    nearest multiple of that spacing, ties to the even multiple (numpy's rint), and the sign is
+    kept (a negative value that rounds to zero gives -0).  The single rounding the GEMM's
+    "one bf16 rounding" asks for ("AstrAI commit log": fused-bias commit) applied to the exact
+    value.  Non-finite input and values that round past the largest bf16 are refused.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise OracleRefusal("non-finite value")
+    ax = np.abs(x)
+    _, ex = np.frexp(ax)                       # ax = m * 2^ex with m in [0.5, 1): e = ex - 1
+    e = np.maximum(ex - 1, -126)
+    step = np.ldexp(1.0, e - 7)
+    v = np.rint(ax / step) * step              # both steps exact: power-of-two scalings
+    if np.any(v >= np.ldexp(1.0, 128)):
+        raise OracleRefusal("value rounds past the largest bf16")
+    f = np.copysign(v, x).astype(np.float32)   # exact: v is a bf16 value
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def gemm_act_quant_ref(a, b, bias=None):
+    """The GEMM whose output is the next layer's activation operand.
+
+    Returns (ref, S, y_bits, codes, scale_bytes): ref and S as gemm_ref; y_bits = the bf16
+    rounding of ref; (codes, scale_bytes) = act_quant(y_bits) per 32 consecutive outputs of a
+    row (the "fp4-gemm README" page's quantizing epilogue idea with this library's activation
+    format).  Any correct GPU bf16 output may differ from y_bits inside the GEMM tolerance, so
+    codes and scale_bytes are exact only for this reference's own rounding; see
+    quant_output_within for the acceptance of a GPU result.
+    """
+    ref, S = gemm_ref(a, b, bias)
+    y = f64_to_bf16_rne(ref)
+    codes, scales = act_quant(y)
+    return ref, S, y, codes, scales
+
+
+def quant_output_within(codes, scale_bytes, ref, S) -> np.ndarray:
+    """Elementwise acceptance of a quantized GEMM output against the exact ref.
+
+    The GPU's bf16 value y satisfies the GEMM bound |y - ref| <= t with t = 2^-7 |ref| + 2^-20 S.
+    act_quant then rounds y / 2^E to E4M3 with no clamping (the scale rule keeps |y| / 2^E <=
+    448): a normal E4M3 value is off by at most half its spacing, 2^-4 of its magnitude, and a
+    subnormal one by at most 2^-10, so |q 2^E - y| <= 2^-4 |y| + 2^(E-10).  Together:
+        |q 2^E - ref| <= 2^-4 (|ref| + t) + t + 2^(E-10).
+    """
+    deq = act_qdq_f64(codes, scale_bytes)
+    ref = np.asarray(ref, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    t = np.ldexp(np.abs(ref), -7) + np.ldexp(S, -20)
+    E = np.repeat(np.asarray(scale_bytes, dtype=np.int64) - 127, BLOCK, axis=-1)
+    bound = np.ldexp(np.abs(ref) + t, -4) + t + np.ldexp(1.0, E - 10)
+    return np.abs(deq - ref) <= bound

@@ -31,8 +31,11 @@ def test_header_declares_the_full_boundary():
     for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
         for v in ("", "_bias", "_strided_batched", "_bias_strided_batched"):
             assert f"mx_gemm_{k}{v}" in names
+    for k in ("fp8_fp4", "fp8_fp8"):
+        for v in ("_quant", "_quant_strided_batched"):
+            assert f"mx_gemm_{k}{v}" in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 16
+    assert len(names) == 20
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -125,6 +128,35 @@ def test_gemm_argument_errors(lib, kind):
     assert gbs(*bargs, 2, 1024, 32, 1024, 32, -1, 256, None) == mx.MX_ERR_STRIDE
     assert gbs(A16, A16, A16, A16, None, A16, 16, 16, 64, 2, 0, 0, 0, 0, 0, 256, None) == \
         mx.MX_ERR_NULL
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8"])
+def test_gemm_quant_argument_errors(lib, kind):
+    g = getattr(lib, f"mx_gemm_{kind}_quant")
+    gs = getattr(lib, f"mx_gemm_{kind}_quant_strided_batched")
+    # a, a_s, b, b_s, bias (may be NULL), q, q_s, M, N, K
+    ok = (A16, A16, A16, A16, None, A16, A16, 16, 64, 64)
+    assert g(*ok[:7], 16, 48, 64, None) == mx.MX_ERR_SHAPE        # N not a multiple of 32
+    assert g(*ok[:7], 16, 64, 48, None) == mx.MX_ERR_SHAPE        # K not a multiple of 32
+    assert g(*ok[:5], None, *ok[6:], None) == mx.MX_ERR_NULL      # q
+    assert g(*ok[:6], None, *ok[7:], None) == mx.MX_ERR_NULL      # q_scale
+    assert g(*ok[:5], A16 + 8, *ok[6:], None) == mx.MX_ERR_ALIGN  # q not 16-byte aligned
+    assert g(*ok[:5], A16, A16 + 1, *ok[7:], None) != mx.MX_ERR_ALIGN
+    assert g(None, None, None, None, None, None, None, 0, 64, 64, None) == mx.MX_OK
+    # batch, sa, sas, sb, sbs, sbias, sq, sqs
+    assert gs(*ok, 2, 1024, 32, 4096, 128, 0, 0, 32, None) == mx.MX_ERR_STRIDE   # q stride 0
+    assert gs(*ok, 2, 1024, 32, 4096, 128, 0, 1024, 0, None) == mx.MX_ERR_STRIDE  # q_s stride 0
+    assert gs(*ok, 2, 1024, 32, 4096, 128, 0, 1032, 32, None) == mx.MX_ERR_ALIGN  # q batch
+    assert gs(*ok, 2, 1024, 32, 4096, 128, -1, 1024, 32, None) == mx.MX_ERR_STRIDE
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8"])
+def test_gemm_quant_valid_args_without_gpu_report_device(lib, kind):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    g = getattr(lib, f"mx_gemm_{kind}_quant")
+    assert g(A16, A16, A16, A16, None, A16, A16, 16, 64, 64, None) == mx.MX_ERR_DEVICE
 
 
 @pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
