@@ -151,7 +151,8 @@ def test_zero_weight_gives_bias_bit_exact(mx, kind):
 # Wide outputs of 448 tiles of 256x256 with ragged M, N and K edges (1.75 waves on 256 CUs).
 WIDE_CASES = [("acts", "fp4", 500, 57267, 224, None, True),
                ("acts", "fp8", 256, 57344, 256, 2, False),
-               ("fp8", "fp4", 511, 57300, 96, None, True)]
+               ("fp8", "fp4", 511, 57300, 96, None, True),
+               ("fp4", "fp4", 300, 57344, 128, None, True)]
 
 
 @pytest.mark.parametrize("a_kind,b_kind,M,N,K,batch,with_bias", WIDE_CASES)
