@@ -9,10 +9,12 @@ E8M0 scales, then the FP8 x MXFP4 GEMM against E2M1 weights [7168, 2048] (per-32
     python bench.py --summarize STATS_DIR FETCH_DIR WRITE_DIR   (CPU only; writes profiles/)
 
 Prints one JSON line.  `value` is the GEMM's 2*M*N*K flops divided by the time of a whole step
-(act_quant included), in TFLOP/s.  `roofline` is the dominant kernel (the GEMM), timed with HIP
-events on the stream it runs on.  `act_quant` reports the standalone producer on [16384, 7168]
-against HBM bandwidth.  `cpu_baseline` times the oracle on a bounded sample of the same workload
-on the host.  --all adds the GEMM kernel time of the other configurations.
+(act_quant included), in TFLOP/s.  `roofline` is the dominant kernel (the GEMM): as many
+back-to-back launches of it as there are steps, on the step's stream and inputs, bracketed by one
+pair of HIP events on that stream.  `act_quant` reports the standalone producer on [16384, 7168]
+against HBM bandwidth, `act_quant_fp4` the MXFP4 producer on the same input.  `cpu_baseline`
+times the oracle on a bounded sample of the same workload on the host.  --all adds the GEMM
+kernel time of the other configurations.
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 METRIC = "block-scaled GEMM TFLOP/s (% MFMA peak) + act_quant GB/s (% HBM peak)"
 ACT_QUANT_BYTES_PER_ELEM = 2 + 1 + 1 / 32      # bf16 in, E4M3 code out, one scale byte per 32
+ACT_QUANT_FP4_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, half a byte of E2M1 out, scale per 32
 
 
 GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip",
@@ -64,16 +68,19 @@ def _traffic(kernel: str, files):
 
 
 def time_events(fn, iters, torch):
-    """Average duration of fn() over iters launches, HIP events on the current stream."""
+    """Average time per fn() over iters back-to-back calls: one pair of HIP events on the current
+    stream (the stream every launch here goes to) brackets the whole run, so the figure is the
+    kernels' own time plus the short gaps between back-to-back dispatches, not the longer gap an
+    event marker between two kernels adds."""
     s = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    for i in range(iters):
-        starts[i].record(s)
-        fn()
-        ends[i].record(s)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / iters   # ms
+    start.record(s)
+    for _ in range(iters):
+        fn()
+    end.record(s)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters   # ms
 
 
 def cpu_baseline(w, rows: int):
@@ -101,7 +108,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true")
@@ -153,19 +160,20 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        mx.mx_act_quant(x, q, s, stream=stream)
-        ev[i][0].record(stream)
-        mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
-        ev[i][1].record(stream)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    gemm_ms = sum(a.elapsed_time(bb) for a, bb in ev) / args.steps
+
+    # the dominant kernel alone: the step's GEMM launched back to back on the same stream and
+    # inputs, as many times as there are steps
+    def gemm():
+        mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
+
+    gemm_ms = time_events(gemm, args.steps, torch)
     flops = 2.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -231,7 +239,31 @@ def main():
                               "unit": "GB/s", "frac": round(aq_gbs / HBM_PEAK_GBS, 4),
                               "traffic": _traffic("act_quant_16384x7168", ACT_QUANT_SOURCES),
                               "algorithmic_bytes_per_launch": aq_bytes}}
-    del xs, qs, ss
+    del qs
+
+    # ---- the MXFP4 producer on the same three input sets (packed E2M1 out, [16384, 3584])
+    q4 = [torch.empty((xs[0].shape[0], xs[0].shape[1] // 2), dtype=torch.uint8, device="cuda")
+          for _ in range(3)]
+    for i in range(6):
+        mx.mx_act_quant_fp4(xs[i % 3], q4[i % 3], ss[i % 3], stream=stream)
+
+    def aq4_launch():
+        i = rot[0] % 3
+        rot[0] += 1
+        mx.mx_act_quant_fp4(xs[i], q4[i], ss[i], stream=stream)
+
+    aq4_ms = time_events(aq4_launch, args.aq_iters, torch)
+    aq4_bytes = ACT_QUANT_FP4_BYTES_PER_ELEM * xs[0].numel()
+    aq4_gbs = aq4_bytes / (aq4_ms * 1e-3) / 1e9
+    act_quant_fp4 = {"workload": "act_quant_fp4 bf16 [16384, 7168] -> packed E2M1 + E8M0 "
+                                 "(3 rotating buffer sets)",
+                     "value": round(aq4_gbs, 1), "unit": "GB/s", "avg_launch_ms": round(aq4_ms, 5),
+                     "roofline": {"bound": "hbm", "achieved": round(aq4_gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(aq4_gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": _traffic("act_quant_fp4_16384x7168", ACT_QUANT_SOURCES),
+                                  "algorithmic_bytes_per_launch": aq4_bytes}}
+    del xs, q4, ss
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
@@ -253,7 +285,7 @@ def main():
            "config": {"workload": "act_quant x[4096,2048] -> FP8xMXFP4 GEMM 4096x7168x2048 + bias",
                       "M": M, "N": N, "K": K, "x_outliers": "1% x100",
                       "weight_scales": "E8M0 118..136", "parallelism": "single GPU"},
-           "roofline": roofline, "act_quant": act_quant,
+           "roofline": roofline, "act_quant": act_quant, "act_quant_fp4": act_quant_fp4,
            "gemm_only_tflops": round(gemm_tflops, 2)}
     out["next_layer_quant"] = next_layer
     if others is not None:
@@ -304,6 +336,63 @@ def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
     return res
 
 
+def _timed_region_averages(stats_dir):
+    """Average kernel-trace duration of the dispatches inside each timed region of a default
+    bench.py run (dispatch order = launch order on the one stream), with the HIP-event average
+    the same run printed for that region."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return {}
+    seq = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                seq.append((int(r["Start_Timestamp"]), r["Kernel_Name"],
+                            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                            int(r["Grid_Size_X"])))
+    seq.sort()
+    line = {}
+    out_txt = os.path.join(stats_dir, "bench_stdout.txt")
+    if os.path.exists(out_txt):
+        with open(out_txt) as fh:
+            js = [ln for ln in fh if ln.startswith("{")]
+        if js:
+            line = json.loads(js[-1])
+    steps, warmup = line.get("steps", 100), line.get("warmup", 200)
+
+    def durs(pattern, grid=None):
+        return [d / 1000.0 for _, k, d, g in seq
+                if re.search(pattern, k) and (grid is None or g == grid)]
+
+    res = {}
+    # the GEMM's dispatches: warm-up steps, timed steps, then the back-to-back GEMM loop
+    gall = durs(r"gemm_bf16_kernel<0, 4, true, false,")
+    g = gall[warmup + steps:warmup + 2 * steps]
+    ev = line.get("roofline", {}).get("avg_launch_ms")
+    if g:
+        res["gemm_fp8_fp4 (back-to-back loop)"] = (len(g), sum(g) / len(g), ev and ev * 1e3)
+    g = gall[warmup:warmup + steps]
+    if g:
+        res["gemm_fp8_fp4 (inside the timed steps)"] = (len(g), sum(g) / len(g), None)
+    big = max((gr for _, k, _, gr in seq if re.search(r"act_quant_kernel<\d+, \w+, 0>", k)),
+              default=None)
+    a8 = durs(r"act_quant_kernel<\d+, \w+, 0>", big)[6:]
+    ev = line.get("act_quant", {}).get("avg_launch_ms")
+    if a8:
+        res["act_quant [16384, 7168]"] = (len(a8), sum(a8) / len(a8), ev and ev * 1e3)
+    a4 = durs(r"act_quant_kernel<\d+, \w+, 4>")[6:]
+    ev = line.get("act_quant_fp4", {}).get("avg_launch_ms")
+    if a4:
+        res["act_quant_fp4 [16384, 7168]"] = (len(a4), sum(a4) / len(a4), ev and ev * 1e3)
+    q = durs(r"gemm_bf16_kernel<0, 4, true, true,")[5:]
+    ev = line.get("next_layer_quant", {}).get("fused_ms")
+    if q:
+        res["gemm_fp8_fp4_quant (fused next layer)"] = (len(q), sum(q) / len(q), ev and ev * 1e3)
+    return res
+
+
 def summarize(stats_dir, fetch_dir, write_dir):
     """Writes the profiles/ summaries from rocprofv3 CSV output of this script:
     kernel-trace stats, and FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same counters
@@ -335,7 +424,8 @@ def summarize(stats_dir, fetch_dir, write_dir):
     write = per_dispatch(write_dir, "WRITE_SIZE")
 
     def pick(vals, name_part, grid=None):
-        v = [b for (k, g, _), b in vals.items() if name_part in k and (grid is None or g == grid)]
+        v = [b for (k, g, _), b in vals.items()
+             if re.search(name_part, k) and (grid is None or g == grid)]
         return sum(v) / len(v) if v else None
 
     def calib(vals):
@@ -350,20 +440,24 @@ def summarize(stats_dir, fetch_dir, write_dir):
     copy_f, copy_w = calib(fetch), calib(write)
     f_factor = copy_f / COPY_BYTES if copy_f else None
     w_factor = copy_w / COPY_BYTES if copy_w else None
-    # act_quant on [16384, 7168]: the act_quant dispatches with the largest grid
-    aq_grids = [g for (k, g, _) in list(fetch) + list(write) if "act_quant_kernel" in k]
+    # act_quant on [16384, 7168]: the act_quant dispatches with the largest grid; the last
+    # template argument of the kernel is the output format (0: E4M3, 4: E2M1)
+    aq8, aq4 = r"act_quant_kernel<\d+, \w+, 0>", r"act_quant_kernel<\d+, \w+, 4>"
+    aq_grids = [g for (k, g, _) in list(fetch) + list(write) if re.search(aq8, k)]
     aq_grid = max(aq_grids) if aq_grids else None
     aq_alg = ACT_QUANT_BYTES_PER_ELEM * 16384 * 7168
+    aq4_alg = ACT_QUANT_FP4_BYTES_PER_ELEM * 16384 * 7168
     gemm_in = 4096 * 2048 + 4096 * 64 + 7168 * 1024 + 7168 * 64 + 2 * 7168
     gemm_alg = gemm_in + 2 * 4096 * 7168
     gemm_q_alg = gemm_in + 4096 * 7168 + 4096 * 7168 // 32
     out = {}
     # template arguments <A format, B format, bias, quantized output, ...> pick the variant
     for name, part, grid, files, alg in (
-            ("act_quant_16384x7168", "act_quant_kernel", aq_grid, ACT_QUANT_SOURCES, aq_alg),
-            ("gemm_fp8_fp4_4096x7168x2048", "gemm_bf16_kernel<0, 4, true, false,", None,
+            ("act_quant_16384x7168", aq8, aq_grid, ACT_QUANT_SOURCES, aq_alg),
+            ("act_quant_fp4_16384x7168", aq4, None, ACT_QUANT_SOURCES, aq4_alg),
+            ("gemm_fp8_fp4_4096x7168x2048", r"gemm_bf16_kernel<0, 4, true, false,", None,
              GEMM_SOURCES, gemm_alg),
-            ("gemm_fp8_fp4_quant_4096x7168x2048", "gemm_bf16_kernel<0, 4, true, true,", None,
+            ("gemm_fp8_fp4_quant_4096x7168x2048", r"gemm_bf16_kernel<0, 4, true, true,", None,
              GEMM_SOURCES, gemm_q_alg)):
         f, w = pick(fetch, part, grid), pick(write, part, grid)
         if f is None or w is None or not f_factor or not w_factor:
@@ -375,31 +469,43 @@ def summarize(stats_dir, fetch_dir, write_dir):
                      "traffic_over_algorithmic": round(hbm / alg, 3)}
         with open(os.path.join(prof, f"traffic_{name}.json"), "w") as fh:
             json.dump(out[name], fh, indent=1)
+    timed = _timed_region_averages(stats_dir)
     cmds = {
-        "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/stats -o run "
-                 "-- python3 bench.py --steps 20 --warmup 5 --no-cpu --aq-iters 20",
-        "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch -o run "
+        "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats -o run "
+                 "-- python3 bench.py --no-cpu > OUT/stats/bench_stdout.txt",
+        "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run "
                  "-- python3 bench.py --steps 2 --warmup 1 --no-cpu --aq-iters 2 --copy-calibration",
-        "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write -o run "
+        "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run "
                  "-- python3 bench.py --steps 2 --warmup 1 --no-cpu --aq-iters 2 --copy-calibration",
-        "summary": "python bench.py --summarize gpurun_out/prof/stats gpurun_out/prof/fetch "
-                   "gpurun_out/prof/write",
+        "summary": "python bench.py --summarize OUT/stats OUT/fetch OUT/write",
     }
-    lines = ["rocprofv3 kernel-trace statistics of one bench.py run (act_quant x[4096,2048] ->",
-             "FP8xMXFP4 GEMM 4096x7168x2048 + bias, 25 steps; plus 20 standalone act_quant",
-             "launches on x[16384,7168] and 5 warm-up launches of it).", "",
-             "command: " + cmds["stats"], "(run from /tmp as TMPDIR, repository root as cwd)", ""]
+    lines = ["rocprofv3 kernel-trace statistics of one bench.py run at its default settings",
+             "(act_quant x[4096,2048] -> FP8xMXFP4 GEMM 4096x7168x2048 + bias, 200 warm-up and 100",
+             "timed steps, then 100 back-to-back launches of the GEMM alone; the fused next-layer",
+             "GEMM and the unfused GEMM + act_quant, 5 warm-up and 50 timed each; 6 warm-up and 50",
+             "timed standalone act_quant launches on x[16384,7168], and as many of the MXFP4",
+             "producer act_quant_fp4).", "",
+             "command: " + cmds["stats"],
+             "(TMPDIR=/tmp, repository root as cwd, OUT the folder the profiler writes to)", ""]
     if stats:
         keys = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "StdDev", "Percentage"]
         lines.append(" | ".join(keys))
         for r in stats:
             lines.append(" | ".join(str(r.get(k, "")) for k in keys))
+    if timed:
+        lines += ["", "Timed-region dispatches only, from the kernel trace of the same run, beside",
+                  "the HIP-event average that run's bench.py line reports for them:"]
+        for name, (n, trace_us, event_us) in timed.items():
+            ev = "n/a" if event_us is None else f"{event_us:.2f} us"
+            lines.append(f"  {name}: {n} dispatches, trace average {trace_us:.2f} us, "
+                         f"events {ev}")
     with open(os.path.join(prof, "kernel_stats_act_quant_and_gemm_fp8_fp4_4096x7168x2048.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     tl = ["HBM traffic per launch from rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE in separate runs),",
           "each scaled by what the same counter reads for a plain 1 GiB device copy",
           f"(FETCH_SIZE/bytes = {f_factor}, WRITE_SIZE/bytes = {w_factor}).", "",
-          "commands:", "  " + cmds["fetch"], "  " + cmds["write"], "  " + cmds["summary"], ""]
+          "commands (OUT: the folder the profiler writes to):", "  " + cmds["fetch"],
+          "  " + cmds["write"], "  " + cmds["summary"], ""]
     for name, d in out.items():
         tl.append(f"{name}: hbm_bytes_per_launch = {d['hbm_bytes_per_launch']}, algorithmic = "
                   f"{d['algorithmic_bytes_per_launch']:.0f}, ratio = {d['traffic_over_algorithmic']} "

@@ -37,6 +37,8 @@ _SIGS = {
     "mx_capability": [ctypes.POINTER(MxCaps)],
     "mx_act_quant": [_P, _P, _P, _I, _I, _P],
     "mx_act_quant_strided_batched": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
+    "mx_act_quant_fp4": [_P, _P, _P, _I, _I, _P],
+    "mx_act_quant_fp4_strided_batched": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
 }
 for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
     _SIGS[f"mx_gemm_{_n}"] = [_P, _P, _P, _P, _P, _I, _I, _I, _P]
@@ -112,6 +114,22 @@ def mx_act_quant_strided_batched(x, q, s, stream=None):
            load().mx_act_quant_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
                                                x.stride(0), q.stride(0), s.stride(0),
                                                _stream(stream)))
+
+
+def mx_act_quant_fp4(x, q, s, stream=None):
+    """x: bf16 [M, K] (cuda); q: uint8 [M, K/2] packed E2M1; s: uint8 [M, K/32] (written)."""
+    M, K = x.shape[-2], x.shape[-1]
+    _check("mx_act_quant_fp4",
+           load().mx_act_quant_fp4(_ptr(x), _ptr(q), _ptr(s), M, K, _stream(stream)))
+
+
+def mx_act_quant_fp4_strided_batched(x, q, s, stream=None):
+    """x: bf16 [B, M, K]; q: uint8 [B, M, K/2]; s: uint8 [B, M, K/32]; strides from the tensors."""
+    B, M, K = x.shape
+    _check("mx_act_quant_fp4_strided_batched",
+           load().mx_act_quant_fp4_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
+                                                   x.stride(0), q.stride(0), s.stride(0),
+                                                   _stream(stream)))
 
 
 def _gemm(kind: str, a, a_s, b, b_s, c, bias=None, K=None, stream=None):

@@ -90,14 +90,14 @@ int validate_act_quant(const void* x, void* q, void* s, int64_t M, int64_t K, in
 }
 
 int act_quant_impl(const void* x, void* q, void* s, int64_t M, int64_t K, int64_t batch,
-                   int64_t sx, int64_t sq, int64_t ss, void* stream) {
+                   int64_t sx, int64_t sq, int64_t ss, void* stream, int fmt = mx::kFp8) {
   int st = validate_act_quant(x, q, s, M, K, batch, sx, sq, ss);
   if (st != MX_OK || M == 0 || batch == 0) return st;
   DeviceInfo dev;
   if ((st = device_status(&dev)) != MX_OK) return st;
   hipError_t e = mx::launch_act_quant(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q),
                                       static_cast<uint8_t*>(s), M, K, batch, sx, sq, ss,
-                                      static_cast<hipStream_t>(stream));
+                                      static_cast<hipStream_t>(stream), fmt);
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
@@ -249,6 +249,16 @@ int mx_act_quant_strided_batched(const void* x, void* q, void* s, int64_t M, int
                                  int64_t batch, int64_t stride_x, int64_t stride_q,
                                  int64_t stride_s, void* stream) {
   return act_quant_impl(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
+}
+
+int mx_act_quant_fp4(const void* x, void* q, void* s, int64_t M, int64_t K, void* stream) {
+  return act_quant_impl(x, q, s, M, K, 1, 0, 0, 0, stream, mx::kFp4);
+}
+
+int mx_act_quant_fp4_strided_batched(const void* x, void* q, void* s, int64_t M, int64_t K,
+                                     int64_t batch, int64_t stride_x, int64_t stride_q,
+                                     int64_t stride_s, void* stream) {
+  return act_quant_impl(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream, mx::kFp4);
 }
 
 #define MX_GEMM_ENTRY_POINTS(NAME, AF, BF)                                                    \

@@ -34,9 +34,10 @@ struct DeviceInfo {
 // Cached per-device properties of the calling thread's current device (false: no device).
 bool current_device(DeviceInfo* info);
 
+// fmt: kFp8 (E4M3 codes [M, K]) or kFp4 (packed E2M1 [M, K/2]); scales E8M0 [M, K/32].
 hipError_t launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
                             int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
-                            hipStream_t stream);
+                            hipStream_t stream, int fmt = kFp8);
 
 // FP8-operand kinds: exact bf16 decode + bf16 MFMA (gemm_bf16.hip).
 hipError_t launch_gemm_bf16(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,

@@ -71,3 +71,37 @@ __device__ __forceinline__ QuantChunk quant_chunk(uint4 w) {
 }
 
 }  // namespace mx
+
+namespace mx {
+
+// The MXFP4 producer of the same 32-blocks: E = ceil(log2(amax / 6)) exactly, where
+// amax = max(max |x|, fp32(1e-4)) = m * 2^e with m in [1, 2): amax / 6 = (m / 1.5) * 2^(e-2) and
+// m / 1.5 lies in [2/3, 4/3), so E = e - 2, plus one when m > 1.5 (mantissa field > 0x400000).
+// x / 2^E then lies in [-6, 6]; v_cvt_scalef32_pk_fp4_f32 divides by the scale 2^E (exact) and
+// rounds to the nearest E2M1 value, ties to the even code, keeping the sign (checked on the device
+// for every bf16 value).  Codes are packed low nibble first: the lane's 8 values give one dword.
+struct QuantChunkFp4 {
+  uint32_t codes;   // 8 E2M1 codes, element 0 in the low nibble
+  uint32_t byte;    // E8M0 byte of the 32-block
+};
+
+__device__ __forceinline__ QuantChunkFp4 quant_chunk_fp4(uint4 w) {
+  const uint32_t amax_bits = quad_max(abs_max_bits(w));
+  const uint32_t ab = __float_as_uint(fmaxf(__uint_as_float(amax_bits << 16), 1e-4f));
+  QuantChunkFp4 r;
+  r.byte = ((ab >> 23) & 0xFFu) - 2u + ((ab & 0x7FFFFFu) > 0x400000u);
+  const float s = __uint_as_float(r.byte << 23);                 // 2^E, a normal fp32
+  uint32_t c = 0;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.x << 16),
+                                               __uint_as_float(w.x & 0xFFFF0000u), s, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.y << 16),
+                                               __uint_as_float(w.y & 0xFFFF0000u), s, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.z << 16),
+                                               __uint_as_float(w.z & 0xFFFF0000u), s, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.w << 16),
+                                               __uint_as_float(w.w & 0xFFFF0000u), s, 3);
+  r.codes = c;
+  return r;
+}
+
+}  // namespace mx

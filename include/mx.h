@@ -91,6 +91,24 @@ int mx_act_quant_strided_batched(const void* x, void* q, void* s, int64_t M, int
                                  int64_t stride_s, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * act_quant_fp4 -- the MXFP4 activation producer (packed E2M1 + per-32 E8M0), the operand format
+ * of the "formats.py" page (FP4_TABLE, low nibble first, one E8M0 byte per 32 values) and of the
+ * "hip_quant PKG-INFO" page's native MXFP4 call.  The pages give no producer rule; this one is
+ * act_quant's with E2M1's largest magnitude 6 in place of 448, per 32 consecutive elements:
+ *   amax = max(max |x|, fp32(1e-4))
+ *   E    = ceil(log2(amax / 6)), exactly (the smallest E with amax <= 6 * 2^E)
+ *   code = E2M1 value nearest x * 2^-E, ties to the even code, sign kept (nothing is clipped)
+ * x  : bf16 [M, K]                (16-byte aligned)
+ * q  : packed E2M1 [M, K/2]       (16-byte aligned; written; element 2j in the low nibble)
+ * s  : E8M0 bytes [M, K/32]       (written)
+ * Bit-exact.  The batched form: batch i at x + i*stride_x, q + i*stride_q, s + i*stride_s.
+ * ------------------------------------------------------------------------------------------- */
+int mx_act_quant_fp4(const void* x, void* q, void* s, int64_t M, int64_t K, void* stream);
+int mx_act_quant_fp4_strided_batched(const void* x, void* q, void* s, int64_t M, int64_t K,
+                                     int64_t batch, int64_t stride_x, int64_t stride_q,
+                                     int64_t stride_s, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Block-scaled GEMM: C[m,n] = bf16_rne( sum_k A[m,k] B[n,k] + bias[n] ), the sum accumulated
  * in fp32 on the matrix cores, the bias (when given) added in fp32 before the one bf16
  * rounding (the "AstrAI commit log" page, fused-bias commit).  Decoded operands:

@@ -373,3 +373,79 @@ def quant_output_within(codes, scale_bytes, ref, S) -> np.ndarray:
     E = np.repeat(np.asarray(scale_bytes, dtype=np.int64) - 127, BLOCK, axis=-1)
     bound = np.ldexp(np.abs(ref) + t, -4) + t + np.ldexp(1.0, E - 10)
     return np.abs(deq - ref) <= bound
+
+
+# ----------------------------------------------------------------------------------------------
+# O5: MXFP4 activation producer (bf16 -> packed E2M1 + per-32 E8M0)
+# ----------------------------------------------------------------------------------------------
+# The pages give the MXFP4 operand format (the formats.py page's FP4_TABLE, nibble order and
+# per-32 E8M0 scales; the hip_quant page's native MXFP4 section) but no rule for producing it
+# from activations.  The rule used here is act_quant's, with E2M1's largest magnitude 6 in
+# place of E4M3's 448 (a reading, listed with the others):
+#   amax = max(max |x|, float32(1e-4)) per 32 consecutive values of a row;
+#   E = ceil(log2(amax / 6)), exactly: the smallest integer with amax <= 6 * 2^E, so every x / 2^E
+#       lies in [-6, 6] and nothing is clipped;
+#   code = the E2M1 value nearest x / 2^E (exact: a power-of-two scaling), ties to the even code,
+#       the sign kept (a negative value that rounds to zero is code 8);
+#   byte = E + 127; codes packed two per byte, element 2j in the low nibble of byte j.
+
+FP4_MAX = 6.0
+
+
+def e2m1_encode_rne(y) -> np.ndarray:
+    """Nearest E2M1 code to each float64 y in [-6, 6], ties to the even code, sign kept.
+
+    The 8 magnitudes are the printed table's codes 0..7 in increasing order ("formats.py":
+    FP4_TABLE); the two candidates around |y| are found by a sorted search, as for E4M3.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(~np.isfinite(y)) or np.any(np.abs(y) > FP4_MAX):
+        raise OracleRefusal("e2m1_encode_rne expects finite |y| <= 6")
+    grid = e2m1_to_f64(np.arange(8, dtype=np.uint8))
+    a = np.abs(y)
+    hi = np.minimum(np.searchsorted(grid, a, side="left"), len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == grid[hi], hi, code).astype(np.uint8)
+    return code | np.where(np.signbit(y), 8, 0).astype(np.uint8)
+
+
+def fp4_pack(codes) -> np.ndarray:
+    """E2M1 codes [..., K] -> packed bytes [..., K/2]: element 2j low nibble, 2j+1 high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def act_scale_fp4_bytes(x_bits) -> np.ndarray:
+    """Per-32 E8M0 bytes of the MXFP4 producer: E + 127 with E = ceil(log2(amax / 6)) exactly.
+
+    amax is taken in float32 as act_scale does (bf16 values are float32 values; the floor is
+    float32(1e-4)).  E starts from floor(log2 amax) - 2 (frexp, exact) and is raised while
+    amax > 6 * 2^E (exact float64 comparisons).
+    """
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    K = x.shape[-1]
+    if K % BLOCK:
+        raise OracleRefusal(f"act_quant_fp4: last dim {K} not a multiple of {BLOCK}")
+    if not np.all(np.isfinite(x)):
+        raise OracleRefusal("act_quant_fp4: non-finite activation")
+    xb = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK))
+    amax = np.maximum(np.abs(xb).max(axis=-1), np.float32(1e-4)).astype(np.float64)
+    _, ex = np.frexp(amax)
+    E = (ex - 1 - 2).astype(np.int64)
+    for _ in range(3):
+        E = E + (amax > FP4_MAX * np.ldexp(1.0, E))
+    return (E + 127).astype(np.uint8)
+
+
+def act_quant_fp4(x_bits) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 activations [..., K] -> (packed E2M1 uint8 [..., K/2], E8M0 bytes uint8 [..., K/32])."""
+    x = bf16_to_f64(x_bits)
+    sb = act_scale_fp4_bytes(x_bits)
+    K = x.shape[-1]
+    y = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK)) / e8m0_to_f64(sb)[..., None]
+    codes = e2m1_encode_rne(y).reshape(x.shape)
+    return fp4_pack(codes), sb

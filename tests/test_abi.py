@@ -28,6 +28,7 @@ def lib():
 def test_header_declares_the_full_boundary():
     names = _declared()
     assert "mx_act_quant" in names and "mx_act_quant_strided_batched" in names
+    assert "mx_act_quant_fp4" in names and "mx_act_quant_fp4_strided_batched" in names
     for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
         for v in ("", "_bias", "_strided_batched", "_bias_strided_batched"):
             assert f"mx_gemm_{k}{v}" in names
@@ -35,7 +36,7 @@ def test_header_declares_the_full_boundary():
         for v in ("_quant", "_quant_strided_batched"):
             assert f"mx_gemm_{k}{v}" in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 20
+    assert len(names) == 22
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -91,6 +92,17 @@ def test_act_quant_argument_errors(lib):
     assert sb(A16, A16, A16, 4, 64, 2, 257, 256, 8, None) == mx.MX_ERR_ALIGN
     assert sb(A16, A16, A16, 4, 64, 70000, 256, 256, 8, None) == mx.MX_ERR_SHAPE
     assert sb(A16, A16, A16, 4, 64, 0, 256, 256, 8, None) == mx.MX_OK
+
+
+def test_act_quant_fp4_argument_errors(lib):
+    f = lib.mx_act_quant_fp4
+    assert f(A16, A16, A16, 4, 48, None) == mx.MX_ERR_SHAPE
+    assert f(None, A16, A16, 4, 64, None) == mx.MX_ERR_NULL
+    assert f(A16, A16 + 4, A16, 4, 64, None) == mx.MX_ERR_ALIGN
+    assert f(None, None, None, 0, 64, None) == mx.MX_OK
+    fb = lib.mx_act_quant_fp4_strided_batched
+    assert fb(A16, A16, A16, 4, 64, 2, 256, 0, 8, None) == mx.MX_ERR_STRIDE
+    assert fb(A16, A16, A16, 4, 64, 2, 256, 136, 8, None) == mx.MX_ERR_ALIGN
 
 
 def test_act_quant_valid_args_without_gpu_report_device(lib):
