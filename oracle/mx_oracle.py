@@ -449,3 +449,64 @@ def act_quant_fp4(x_bits) -> tuple[np.ndarray, np.ndarray]:
     y = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK)) / e8m0_to_f64(sb)[..., None]
     codes = e2m1_encode_rne(y).reshape(x.shape)
     return fp4_pack(codes), sb
+
+
+# ----------------------------------------------------------------------------------------------
+# O6: residual and GELU epilogues
+# ----------------------------------------------------------------------------------------------
+# The "fp4-gemm README" page lists GEMM epilogues that add a residual (bias + residual, and
+# residual alone) or apply GELU after the bias, so that the output feeds the next low-bit GEMM
+# without a separate elementwise pass; it gives no formula for either.  Readings used here (each
+# is listed with the others):
+#   residual: out = one bf16 rounding of (sum_k a*b + bias[n] + residual[m, n]); the residual is
+#       a bf16 [M, N] tensor added before the single rounding, like the bias;
+#   GELU: the exact form x * Phi(x), Phi the standard normal CDF, applied to (sum_k a*b + bias[n])
+#       before the single rounding.
+
+GELU_LIPSCHITZ = 1.128905                # >= max |d/dx x Phi(x)| = Phi(sqrt 2) + sqrt 2 phi(sqrt 2)
+
+
+def gelu_f64(x) -> np.ndarray:
+    """x * Phi(x) in float64, written as 0.5 x erfc(-x / sqrt 2).
+
+    erfc (the library routine) rather than 1 + erf keeps the relative accuracy where Phi(x) is
+    tiny (large negative x), where 1 + erf(x / sqrt 2) would cancel.
+    """
+    from scipy.special import erfc
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * erfc(-x / np.sqrt(2.0))
+
+
+def gemm_residual_ref(a, b, bias=None, residual_bits=None) -> tuple[np.ndarray, np.ndarray]:
+    """(ref, S): gemm_ref with the bf16 residual [..., M, N] added to the unrounded value.
+
+    The residual enters like the bias, before the single bf16 rounding, so the GEMM acceptance
+    bound applies unchanged to out against this ref.
+    """
+    ref, S = gemm_ref(a, b, bias)
+    if residual_bits is not None:
+        ref = ref + bf16_to_f64(residual_bits)
+    return ref, S
+
+
+def gemm_gelu_ref(a, b, bias=None) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(g, pre, S): g = gelu_f64(pre), pre = sum_k a*b + bias (gemm_ref), S = sum_k |a*b|."""
+    pre, S = gemm_ref(a, b, bias)
+    return gelu_f64(pre), pre, S
+
+
+def gelu_within(out_bits, pre, S) -> np.ndarray:
+    """Elementwise acceptance of a bf16 GELU output against the exact pre-activation value pre.
+
+    The GPU accumulator a meets the GEMM's accuracy, |a - pre| <= 2^-20 S; GELU is Lipschitz with
+    constant GELU_LIPSCHITZ < 2, so |gelu(a) - gelu(pre)| <= 2^-19 S; the float32 evaluation of
+    GELU and the one bf16 rounding add at most 2^-7 |gelu(pre)| (bf16 alone is 2^-9); values in
+    the bf16 subnormal range are resolved to 2^-126 at best.  Accepted when
+        |out - gelu(pre)| <= 2^-7 |gelu(pre)| + 2^-19 S + 2^-126.
+    A NaN or infinite output is never accepted.
+    """
+    out = bf16_to_f64(out_bits)
+    g = gelu_f64(pre)
+    S = np.asarray(S, dtype=np.float64)
+    ok = np.abs(out - g) <= np.ldexp(np.abs(g), -7) + np.ldexp(S, -19) + np.ldexp(1.0, -126)
+    return ok & np.isfinite(out)
