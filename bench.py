@@ -39,6 +39,7 @@ ACT_QUANT_FP4_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, half a byte of E2M1
 
 
 GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip",
+                "block_scaled_precision_act_amd/csrc/mx_epilogue.h",
                 "block_scaled_precision_act_amd/csrc/mx_quant.h"]
 ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip",
                      "block_scaled_precision_act_amd/csrc/mx_quant.h"]
@@ -211,6 +212,29 @@ def main():
                   "fused_traffic": _traffic("gemm_fp8_fp4_quant_4096x7168x2048", GEMM_SOURCES)}
     del qn, qsn
 
+    # ---- the residual and GELU epilogues on the same GEMM (bf16 out), against the plain bias one
+    res_t = torch.empty((M, N), dtype=torch.bfloat16, device="cuda").normal_()
+
+    def with_residual():
+        mx.mx_gemm_fp8_fp4_bias_residual(q, s, b, b_s, res_t, c, bias=bias, stream=stream)
+
+    def with_gelu():
+        mx.mx_gemm_fp8_fp4_bias_gelu(q, s, b, b_s, c, bias=bias, stream=stream)
+
+    for _ in range(5):
+        with_residual()
+        with_gelu()
+    res_ms = time_events(with_residual, 50, torch)
+    gelu_ms = time_events(with_gelu, 50, torch)
+    epilogues = {"workload": "FP8xMXFP4 GEMM 4096x7168x2048 + bias, bf16 out: + bf16 residual "
+                             "[4096, 7168], or GELU",
+                 "bias_ms": round(gemm_ms, 5),
+                 "bias_residual_ms": round(res_ms, 5),
+                 "bias_residual_tflops": round(flops / (res_ms * 1e-3) / 1e12, 2),
+                 "bias_gelu_ms": round(gelu_ms, 5),
+                 "bias_gelu_tflops": round(flops / (gelu_ms * 1e-3) / 1e12, 2)}
+    del res_t
+
     # ---- standalone act_quant on [16384, 7168], sustained: back-to-back launches rotating over
     # three input/output sets (1.07 GB, far beyond the 256 MB last-level cache), so each launch
     # reads its input from HBM and pays for the previous launch's write-back.
@@ -288,6 +312,7 @@ def main():
            "roofline": roofline, "act_quant": act_quant, "act_quant_fp4": act_quant_fp4,
            "gemm_only_tflops": round(gemm_tflops, 2)}
     out["next_layer_quant"] = next_layer
+    out["epilogues"] = epilogues
     if others is not None:
         out["other_configs"] = others
     if not args.no_cpu:
@@ -296,10 +321,47 @@ def main():
 
 
 def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
-    """GEMM kernel time of the other configurations (operands already quantized in HBM)."""
-    res = {}
+    """GEMM kernel time of the other configurations (operands already quantized in HBM).
 
-    def run(w, kind, bias=True):
+    For each: `ms` over back-to-back launches on the stream (one event pair around the run).
+    The latency-bound ones (the 16x256x512 and 1024^3 configurations and the A4W4 shapes) also
+    report `graph_ms`, the time per launch of 20 launches captured in one HIP graph and replayed
+    (launch overhead amortized), and `cold_ms`, the median time of single launches each after
+    512 MB were written to evict the caches (events around the GEMM alone).  The A4W4 shapes
+    also time their residual and GELU epilogues."""
+    res = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def graph_ms(launch, reps=20, iters=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                launch(None)                  # the capture stream is the current stream
+        g.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(cur)
+        for _ in range(iters):
+            g.replay()
+        end.record(cur)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / (iters * reps)
+
+    def cold_ms(launch, iters=10):
+        cur = torch.cuda.current_stream()
+        ts = []
+        for i in range(iters):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            launch(stream)
+            b.record(cur)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    def run(w, kind, bias=True, latency=False, epilogues=False):
         if w.a_kind == "acts":
             xq = dev_bf16(w.x)
             shape = xq.shape
@@ -317,22 +379,45 @@ def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
         shape = (w.M, w.N) if w.batch is None else (w.batch, w.M, w.N)
         c = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
         fn = getattr(mx, f"mx_gemm_{kind}")
-        for _ in range(3):
-            fn(a, a_s, b, b_s, c, bias=bias_t, stream=stream)
-        ms = time_events(lambda: fn(a, a_s, b, b_s, c, bias=bias_t, stream=stream), 20, torch)
-        flops = 2.0 * w.M * w.N * w.K * (w.batch or 1)
-        return {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
-    res["fp8xmxfp4_16x256x512"] = run(synth.fp8xmxfp4_16x256x512(), "fp8_fp4")
-    res["fp8xfp8_1024^3_bias"] = run(synth.fp8xfp8_1024cubed_bias(), "fp8_fp8")
+        def launch(st):
+            fn(a, a_s, b, b_s, c, bias=bias_t, stream=st)
+
+        # warm up for about 50 ms of launches (past the clock drop sustained load brings)
+        rough = time_events(lambda: launch(stream), 3, torch)
+        for _ in range(max(3, int(50.0 / max(rough, 1e-3)))):
+            launch(stream)
+        ms = time_events(lambda: launch(stream), 20, torch)
+        flops = 2.0 * w.M * w.N * w.K * (w.batch or 1)
+        r = {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        if latency:
+            r["graph_ms"] = round(graph_ms(launch), 5)
+            r["cold_ms"] = round(cold_ms(launch), 5)
+        if epilogues:
+            resid = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_()
+            fr = getattr(mx, f"mx_gemm_{kind}_bias_residual")
+            fg = getattr(mx, f"mx_gemm_{kind}_bias_gelu")
+            for _ in range(3):
+                fr(a, a_s, b, b_s, resid, c, bias=bias_t, stream=stream)
+                fg(a, a_s, b, b_s, c, bias=bias_t, stream=stream)
+            r["bias_residual_ms"] = round(time_events(
+                lambda: fr(a, a_s, b, b_s, resid, c, bias=bias_t, stream=stream), 20, torch), 5)
+            r["bias_gelu_ms"] = round(time_events(
+                lambda: fg(a, a_s, b, b_s, c, bias=bias_t, stream=stream), 20, torch), 5)
+        return r
+
+    res["fp8xmxfp4_16x256x512"] = run(synth.fp8xmxfp4_16x256x512(), "fp8_fp4", latency=True)
+    res["fp8xfp8_1024^3_bias"] = run(synth.fp8xfp8_1024cubed_bias(), "fp8_fp8", latency=True)
     for i in range(3):
         w = synth.a4w4_skinny(i)
-        r = run(w, "fp4_fp4")
+        r = run(w, "fp4_fp4", latency=True, epilogues=True)
         nbytes = w.M * w.K / 2 + w.M * w.K / 32 + w.N * w.K / 2 + w.N * w.K / 32 + 2 * w.M * w.N
         r["gbs"] = round(nbytes / (r["ms"] * 1e-3) / 1e9, 1)
+        r["graph_gbs"] = round(nbytes / (r["graph_ms"] * 1e-3) / 1e9, 1)
         res[w.name] = r
     res["fp8xfp8_8x1024x2048x2048"] = run(synth.fp8xfp8_batched_8x1024x2048x2048(), "fp8_fp8")
     res["fp8xfp8_8192^3"] = run(synth.fp8xfp8_8192cubed(), "fp8_fp8")
+    del flush
     return res
 
 

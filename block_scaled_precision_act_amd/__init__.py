@@ -47,6 +47,13 @@ for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
                                               _I, _I, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_bias_strided_batched"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                                    _I, _I, _I, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_bias_residual"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_bias_residual_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                                            _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                                            _P]
+    _SIGS[f"mx_gemm_{_n}_bias_gelu"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_bias_gelu_strided_batched"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                                        _I, _I, _I, _I, _I, _I, _P]
 for _n in ("fp8_fp4", "fp8_fp8"):
     _SIGS[f"mx_gemm_{_n}_quant"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_quant_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -208,3 +215,57 @@ def mx_gemm_fp8_fp4_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
 def mx_gemm_fp8_fp8_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
     """As mx_gemm_fp8_fp4_quant with b: E4M3 [(B,) N, K] and b_s: [(B,) ceil(N/32), K/32]."""
     _gemm_quant("fp8_fp8", a, a_s, b, b_s, q, q_s, bias, stream)
+
+
+def _gemm_epilogue(kind: str, epi: str, a, a_s, b, b_s, c, bias=None, residual=None,
+                   stream=None):
+    M, N = c.shape[-2], c.shape[-1]
+    K = a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+    lib = load()
+    st = _stream(stream)
+    res = [_ptr(residual)] if epi == "residual" else []
+    if c.dim() == 2:
+        name = f"mx_gemm_{kind}_bias_{epi}"
+        r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), *res, _ptr(c),
+                               M, N, K, st)
+    else:
+        B = c.shape[0]
+        strides = [t.stride(0) if t.dim() == 3 else 0 for t in (a, a_s, b, b_s)]
+        sbias = bias.stride(0) if (bias is not None and bias.dim() == 2) else 0
+        sres = [residual.stride(0) if residual.dim() == 3 else 0] if epi == "residual" else []
+        name = f"mx_gemm_{kind}_bias_{epi}_strided_batched"
+        r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), *res, _ptr(c),
+                               M, N, K, B, *strides, sbias, *sres, c.stride(0), st)
+    _check(name, r)
+
+
+def mx_gemm_fp8_fp4_bias_residual(a, a_s, b, b_s, residual, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4 with a bf16 residual [(B,) M, N] added before the one bf16 rounding
+    (residual may be c itself); bias optional."""
+    _gemm_epilogue("fp8_fp4", "residual", a, a_s, b, b_s, c, bias, residual, stream)
+
+
+def mx_gemm_fp8_fp8_bias_residual(a, a_s, b, b_s, residual, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_bias_residual for FP8 weights."""
+    _gemm_epilogue("fp8_fp8", "residual", a, a_s, b, b_s, c, bias, residual, stream)
+
+
+def mx_gemm_fp4_fp4_bias_residual(a, a_s, b, b_s, residual, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_bias_residual for MXFP4 activations."""
+    _gemm_epilogue("fp4_fp4", "residual", a, a_s, b, b_s, c, bias, residual, stream)
+
+
+def mx_gemm_fp8_fp4_bias_gelu(a, a_s, b, b_s, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4 with GELU (x * Phi(x)) applied to sum + bias before the one bf16
+    rounding; bias optional."""
+    _gemm_epilogue("fp8_fp4", "gelu", a, a_s, b, b_s, c, bias, None, stream)
+
+
+def mx_gemm_fp8_fp8_bias_gelu(a, a_s, b, b_s, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_bias_gelu for FP8 weights."""
+    _gemm_epilogue("fp8_fp8", "gelu", a, a_s, b, b_s, c, bias, None, stream)
+
+
+def mx_gemm_fp4_fp4_bias_gelu(a, a_s, b, b_s, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_bias_gelu for MXFP4 activations."""
+    _gemm_epilogue("fp4_fp4", "gelu", a, a_s, b, b_s, c, bias, None, stream)

@@ -32,9 +32,11 @@
 //   * the workgroup -> tile map keeps consecutive tiles on one XCD (workgroups are dealt to the 8
 //     XCDs round-robin) and walks them in groups of kGroupM tile rows, so an XCD's L2 holds the
 //     A rows and B rows its running tiles share;
-//   * epilogue: fp32 + bias, one RNE rounding, staged through LDS for 16-byte row stores; or, for
-//     the quantizing entry points, the same bf16 tile quantized per 32 columns to E4M3 + E8M0
-//     (the next layer's activation operand) without writing the bf16 values out.
+//   * epilogue: fp32 + bias (+ a bf16 residual, or GELU), one RNE rounding, staged through LDS
+//     for 16-byte row stores; or, for the quantizing entry points, the same bf16 tile quantized
+//     per 32 columns to E4M3 + E8M0 (the next layer's activation operand) without writing the
+//     bf16 values out.
+#include "mx_epilogue.h"
 #include "mx_internal.h"
 #include "mx_quant.h"
 
@@ -75,6 +77,8 @@ struct Args {
   uint8_t* q;
   uint8_t* qs;
   int64_t stride_q, stride_qs;
+  const uint16_t* res;
+  int64_t stride_res;
 };
 
 // fp32 value of an E8M0 byte (2^(b-127)); byte 0 is the fp32 subnormal 2^-127.
@@ -431,7 +435,10 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
 
 // QUANT: instead of the bf16 output, write its per-32 E4M3 codes and E8M0 bytes (the next
 // layer's activation operand), computed from the same bf16 values with the act_quant arithmetic.
-template <int AF, int BF, bool BIAS, bool QUANT, int BM, int BN, int WM, int WN>
+// EPI (bf16 output only): kEpiResidual adds the bf16 residual [M, N] before the rounding,
+// kEpiGelu applies GELU to (sum + bias); both take the bias pointer as optional (BIAS is true
+// for them and a null bias adds nothing).
+template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;     // WM x WN wavefronts
@@ -521,30 +528,65 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   // copied out in coalesced 16-byte row segments.
   __syncthreads();                       // every wavefront is done reading the operand stages
   constexpr int kTileRow = BN * 2;       // bytes of one bf16 tile row
+  constexpr int kChunksPerRow = BN / 8;
+  if constexpr (EPI == kEpiResidual) {
+    // The residual tile is first copied into the LDS tile in the same layout, with coalesced
+    // 16-byte loads (zeros outside the matrix); each thread below reads the residual at its own
+    // outputs' places and overwrites them with the results.  The residual may be the output
+    // itself: every read of the tile precedes the barrier before the copy-out.
+    const uint16_t* res = p.res + bz * p.stride_res;
+    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+      const int row = m0 + trow, col = n0 + tch * 8;
+      const int ch = tch ^ (((trow >> 2) & 1) << 2);
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (row < p.M && col < p.N) {
+        const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
+        if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+          v = *reinterpret_cast<const uint4*>(src);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) e[k] = col + k < p.N ? src[k] : 0u;
+          v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                    e[6] | (e[7] << 16)};
+        }
+      }
+      *reinterpret_cast<uint4*>(lds + trow * kTileRow + ch * 16) = v;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int tcol = wn * WTN + 32 * j + l32;
     float bias = 0.0f;
-    if (BIAS) {
+    if (BIAS && (EPI == kEpiPlain || p.bias != nullptr)) {
       const int col = min(n0 + tcol, p.N - 1);
-      bias = __uint_as_float(static_cast<uint32_t>(p.bias[bz * p.stride_bias + col]) << 16);
+      bias = bf16_bits_to_f32(p.bias[bz * p.stride_bias + col]);
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const int trow = wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);   // rows trow, trow+1
-        bf16x2 pk = {static_cast<__bf16>(acc[i][j][r] + bias), static_cast<__bf16>(acc[i][j][r + 1] + bias)};
-        const uint32_t w = pk_bits(pk);
         const int ch = (tcol >> 3) ^ (((trow >> 2) & 1) << 2);
         const uint32_t off = static_cast<uint32_t>(trow * kTileRow + ch * 16 + (tcol & 7) * 2);
+        float v0 = acc[i][j][r] + bias, v1 = acc[i][j][r + 1] + bias;
+        if constexpr (EPI == kEpiResidual) {
+          v0 += bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + off));
+          v1 += bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + off + kTileRow));
+        } else if constexpr (EPI == kEpiGelu) {
+          v0 = gelu_f32(v0);
+          v1 = gelu_f32(v1);
+        }
+        bf16x2 pk = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
+        const uint32_t w = pk_bits(pk);
         *reinterpret_cast<uint16_t*>(lds + off) = static_cast<uint16_t>(w & 0xFFFFu);
         *reinterpret_cast<uint16_t*>(lds + off + kTileRow) = static_cast<uint16_t>(w >> 16);
       }
     }
   }
   __syncthreads();
-  constexpr int kChunksPerRow = BN / 8;
   if constexpr (QUANT) {
     // Four consecutive lanes hold the four 16-byte chunks of one 32-column block of a row
     // (kChunksPerRow % 4 == 0), and every lane of the workgroup runs every iteration (the tile's
@@ -594,11 +636,11 @@ constexpr int lds_bytes() {
   return stages > tile ? stages : tile;
 }
 
-template <int AF, int BF, bool BIAS, bool QUANT, int BM, int BN, int WM, int WN>
+template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN>
 hipError_t launch_kernel(const Args& p, dim3 grid, hipStream_t stream) {
   constexpr int kLds = lds_bytes<AF, BF, BM, BN>();
   static_assert(kLds <= 160 * 1024, "LDS");
-  auto k = gemm_bf16_kernel<AF, BF, BIAS, QUANT, BM, BN, WM, WN>;
+  auto k = gemm_bf16_kernel<AF, BF, BIAS, QUANT, EPI, BM, BN, WM, WN>;
   // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
   static const hipError_t attr_ok = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
@@ -612,16 +654,20 @@ hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
-         g.q, g.qs, g.stride_q, g.stride_qs};
+         g.q, g.qs, g.stride_q, g.stride_qs, g.residual, g.stride_res};
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
   if constexpr (AF == kFp8) {
     if (g.q) {
-      return g.bias ? launch_kernel<AF, BF, true, true, BM, BN, WM, WN>(p, grid, stream)
-                    : launch_kernel<AF, BF, false, true, BM, BN, WM, WN>(p, grid, stream);
+      return g.bias ? launch_kernel<AF, BF, true, true, kEpiPlain, BM, BN, WM, WN>(p, grid, stream)
+                    : launch_kernel<AF, BF, false, true, kEpiPlain, BM, BN, WM, WN>(p, grid, stream);
     }
   }
-  return g.bias ? launch_kernel<AF, BF, true, false, BM, BN, WM, WN>(p, grid, stream)
-                : launch_kernel<AF, BF, false, false, BM, BN, WM, WN>(p, grid, stream);
+  if (g.epi == kEpiResidual)
+    return launch_kernel<AF, BF, true, false, kEpiResidual, BM, BN, WM, WN>(p, grid, stream);
+  if (g.epi == kEpiGelu)
+    return launch_kernel<AF, BF, true, false, kEpiGelu, BM, BN, WM, WN>(p, grid, stream);
+  return g.bias ? launch_kernel<AF, BF, true, false, kEpiPlain, BM, BN, WM, WN>(p, grid, stream)
+                : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN>(p, grid, stream);
 }
 
 template <int AF, int BF>

@@ -6,7 +6,9 @@
 //
 // C[m,n] = bf16_rne(sum_k A[m,k] B[n,k] + bias[n]) with fp32 accumulation on the matrix cores
 // ("formats.py" page: decode_fp4 / decode_fp8_block / act_qdq give the decoded operands;
-// "AstrAI commit log" page: the bias is added in fp32 before the single bf16 rounding).
+// "AstrAI commit log" page: the bias is added in fp32 before the single bf16 rounding), or with
+// a bf16 residual added, or GELU applied, before that rounding.
+#include "mx_epilogue.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -24,6 +26,8 @@ struct Args {
   uint16_t* c;
   int M, N, K;
   int64_t stride_a, stride_as, stride_b, stride_bs, stride_bias, stride_c;
+  const uint16_t* res;
+  int64_t stride_res;
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float v) {
@@ -50,7 +54,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-template <int MT, int W, int G, bool BIAS>
+template <int MT, int W, int G, bool BIAS, int EPI>
 __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
   __shared__ v4f red[W][MT][64];
   const int lane = threadIdx.x & 63;
@@ -132,12 +136,20 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
     const int c = n0 + r16;
     if (c < p.N) {
       float bias = 0.0f;
-      if (BIAS) bias = __uint_as_float(static_cast<uint32_t>(p.bias[bz * p.stride_bias + c]) << 16);
+      if (BIAS && (EPI == kEpiPlain || p.bias != nullptr))
+        bias = bf16_bits_to_f32(p.bias[bz * p.stride_bias + c]);
       uint16_t* out = p.c + bz * p.stride_c;
+      const uint16_t* res = p.res + bz * p.stride_res;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * t + 4 * g + r;
-        if (row < p.M) out[static_cast<int64_t>(row) * p.N + c] = to_bf16(sum[r] + bias);
+        if (row >= p.M) continue;
+        const int64_t at = static_cast<int64_t>(row) * p.N + c;
+        float v = sum[r] + bias;
+        // the residual may be the output itself: this thread reads it before writing it
+        if constexpr (EPI == kEpiResidual) v += bf16_bits_to_f32(res[at]);
+        if constexpr (EPI == kEpiGelu) v = gelu_f32(v);
+        out[at] = to_bf16(v);
       }
     }
   }
@@ -146,12 +158,22 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
 template <int MT, int W, int G>
 hipError_t launch_skinny(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
-         g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c};
+         g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
+         g.residual, g.stride_res};
   dim3 grid((g.N + 15) / 16, g.batch);
-  if (g.bias)
-    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true>), grid, dim3(64 * W), 0, stream, p);
+  const dim3 block(64 * W);
+  if (g.epi == kEpiResidual)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true, kEpiResidual>), grid, block, 0,
+                       stream, p);
+  else if (g.epi == kEpiGelu)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true, kEpiGelu>), grid, block, 0,
+                       stream, p);
+  else if (g.bias)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true, kEpiPlain>), grid, block, 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, false>), grid, dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, false, kEpiPlain>), grid, block, 0,
+                       stream, p);
   return hipGetLastError();
 }
 

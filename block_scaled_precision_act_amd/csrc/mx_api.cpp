@@ -113,6 +113,10 @@ struct GemmCall {
   void* q = nullptr;
   void* qs = nullptr;
   int64_t sq = 0, sqs = 0;
+  // Epilogue (bf16 output only): mx::kEpiResidual adds res [M, N]; mx::kEpiGelu applies GELU.
+  int epi = mx::kEpiPlain;
+  const void* res = nullptr;
+  int64_t sres = 0;
 };
 
 int validate_gemm(const GemmCall& g) {
@@ -123,13 +127,14 @@ int validate_gemm(const GemmCall& g) {
   if (g.M > 0 && g.N > 0 && g.M > mx::kMaxMatrixElems / g.N) return MX_ERR_SHAPE;
   if (g.quant && g.N % 32 != 0) return MX_ERR_SHAPE;
   if (g.sa < 0 || g.sas < 0 || g.sb < 0 || g.sbs < 0 || g.sbias < 0 || g.sc < 0 || g.sq < 0 ||
-      g.sqs < 0)
+      g.sqs < 0 || g.sres < 0)
     return MX_ERR_STRIDE;
   if (g.batch > 1 && (g.quant ? (g.sq == 0 || g.sqs == 0) : g.sc == 0)) return MX_ERR_STRIDE;
   if (g.M == 0 || g.N == 0 || g.batch == 0) return MX_OK;
   if (!g.a || !g.a_s || !g.b || !g.b_s) return MX_ERR_NULL;
   if (g.quant ? (!g.q || !g.qs) : !g.c) return MX_ERR_NULL;
   if (g.needs_bias && !g.bias) return MX_ERR_NULL;
+  if (g.epi == mx::kEpiResidual && !g.res) return MX_ERR_NULL;
   if (!mx::aligned16(g.a) || !mx::aligned16(g.b)) return MX_ERR_ALIGN;
   if (g.sa % 16 != 0 || g.sb % 16 != 0) return MX_ERR_ALIGN;
   if (g.quant && (!mx::aligned16(g.q) || g.sq % 16 != 0)) return MX_ERR_ALIGN;
@@ -158,6 +163,9 @@ int gemm_impl(const GemmCall& g, void* stream) {
   p.stride_bs = g.sbs;
   p.stride_bias = g.sbias;
   p.stride_c = g.sc;
+  p.epi = g.epi;
+  p.residual = static_cast<const uint16_t*>(g.res);
+  p.stride_res = g.sres;
   if (g.quant) {
     p.c = nullptr;
     p.q = static_cast<uint8_t*>(g.q);
@@ -180,6 +188,13 @@ GemmCall batched(int af, int bf, const void* a, const void* a_s, const void* b, 
                  bool needs_bias) {
   return GemmCall{af, bf, a, a_s, b, b_s, bias, c, M, N, K, batch,
                   sa, sas, sb, sbs, sbias, sc, needs_bias};
+}
+
+GemmCall with_epilogue(GemmCall g, int epi, const void* res, int64_t sres) {
+  g.epi = epi;
+  g.res = res;
+  g.sres = sres;
+  return g;
 }
 
 GemmCall quantized(int af, int bf, const void* a, const void* a_s, const void* b,
@@ -316,5 +331,47 @@ MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp4, mx::kFp8, mx::kFp4)
 MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
 
 #undef MX_GEMM_QUANT_ENTRY_POINTS
+
+// The bias is optional (NULL adds nothing) in the residual and GELU entry points.
+#define MX_GEMM_EPILOGUE_ENTRY_POINTS(NAME, AF, BF)                                           \
+  int mx_gemm_##NAME##_bias_residual(const void* a, const void* a_s, const void* b,           \
+                                     const void* b_s, const void* bias, const void* residual, \
+                                     void* c, int64_t M, int64_t N, int64_t K, void* stream) { \
+    return gemm_impl(with_epilogue(single(AF, BF, a, a_s, b, b_s, bias, c, M, N, K, false),   \
+                                   mx::kEpiResidual, residual, 0),                            \
+                     stream);                                                                 \
+  }                                                                                           \
+  int mx_gemm_##NAME##_bias_residual_strided_batched(                                         \
+      const void* a, const void* a_s, const void* b, const void* b_s, const void* bias,       \
+      const void* residual, void* c, int64_t M, int64_t N, int64_t K, int64_t batch,          \
+      int64_t sa, int64_t sas, int64_t sb, int64_t sbs, int64_t sbias, int64_t sres,          \
+      int64_t sc, void* stream) {                                                             \
+    return gemm_impl(with_epilogue(batched(AF, BF, a, a_s, b, b_s, bias, c, M, N, K, batch,   \
+                                           sa, sas, sb, sbs, sbias, sc, false),               \
+                                   mx::kEpiResidual, residual, sres),                         \
+                     stream);                                                                 \
+  }                                                                                           \
+  int mx_gemm_##NAME##_bias_gelu(const void* a, const void* a_s, const void* b,               \
+                                 const void* b_s, const void* bias, void* c, int64_t M,       \
+                                 int64_t N, int64_t K, void* stream) {                        \
+    return gemm_impl(with_epilogue(single(AF, BF, a, a_s, b, b_s, bias, c, M, N, K, false),   \
+                                   mx::kEpiGelu, nullptr, 0),                                 \
+                     stream);                                                                 \
+  }                                                                                           \
+  int mx_gemm_##NAME##_bias_gelu_strided_batched(                                             \
+      const void* a, const void* a_s, const void* b, const void* b_s, const void* bias,       \
+      void* c, int64_t M, int64_t N, int64_t K, int64_t batch, int64_t sa, int64_t sas,       \
+      int64_t sb, int64_t sbs, int64_t sbias, int64_t sc, void* stream) {                     \
+    return gemm_impl(with_epilogue(batched(AF, BF, a, a_s, b, b_s, bias, c, M, N, K, batch,   \
+                                           sa, sas, sb, sbs, sbias, sc, false),               \
+                                   mx::kEpiGelu, nullptr, 0),                                 \
+                     stream);                                                                 \
+  }
+
+MX_GEMM_EPILOGUE_ENTRY_POINTS(fp8_fp4, mx::kFp8, mx::kFp4)
+MX_GEMM_EPILOGUE_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
+MX_GEMM_EPILOGUE_ENTRY_POINTS(fp4_fp4, mx::kFp4, mx::kFp4)
+
+#undef MX_GEMM_EPILOGUE_ENTRY_POINTS
 
 }  // extern "C"

@@ -9,6 +9,13 @@ namespace mx {
 // Operand encodings, numbered as the scaled f8f6f4 MFMA's format fields number them.
 enum OperandFmt : int { kFp8 = 0, kFp4 = 4 };
 
+// What the epilogue does to (sum + bias) before the single bf16 rounding.
+enum Epilogue : int {
+  kEpiPlain = 0,      // nothing
+  kEpiResidual = 1,   // + residual[m, n] (bf16 [M, N])
+  kEpiGelu = 2,       // x * Phi(x)
+};
+
 // One validated GEMM problem.  Per-matrix element counts are < 2^31; batch strides are in
 // elements of each buffer (bytes for codes / packed / scales, bf16 elements for bias and c).
 struct GemmProblem {
@@ -23,6 +30,9 @@ struct GemmProblem {
   uint8_t* q = nullptr;   // E4M3 codes of the bf16 output [M, N] (N % 32 == 0)
   uint8_t* qs = nullptr;  // their E8M0 bytes [M, N/32]
   int64_t stride_q = 0, stride_qs = 0;
+  int epi = kEpiPlain;    // kEpiResidual / kEpiGelu: bf16 output only (q == nullptr)
+  const uint16_t* residual = nullptr;   // kEpiResidual: bf16 [M, N], may be c itself
+  int64_t stride_res = 0;
 };
 
 struct DeviceInfo {

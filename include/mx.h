@@ -221,6 +221,88 @@ int mx_gemm_fp8_fp8_quant_strided_batched(const void* a, const void* a_scale, co
                                           int64_t stride_bias, int64_t stride_q,
                                           int64_t stride_q_scale, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * GEMM with a residual or GELU epilogue (bf16 output).
+ *
+ * The "fp4-gemm README" page lists bias + residual and bias + GELU GEMM epilogues (API list; the
+ * paragraph on avoiding a return to bf16 elementwise code between low-bit GEMMs) without a
+ * formula.  Here, with s[m,n] = sum_k A[m,k] B[n,k] (fp32 accumulation) and bias optional:
+ *   _bias_residual:  c[m,n] = bf16_rne( s[m,n] + bias[n] + residual[m,n] )
+ *   _bias_gelu:      c[m,n] = bf16_rne( gelu(s[m,n] + bias[n]) ),  gelu(x) = x * Phi(x) with Phi
+ *                    the standard normal CDF (the exact form, not the tanh approximation)
+ * one bf16 rounding each, all additions in fp32.
+ *   bias      bf16 [N], or NULL (adds nothing)
+ *   residual  bf16 [M, N] row-major (must not be NULL); it may be c itself (the same pointer and
+ *             batch stride: an in-place residual add); any other overlap with c is undefined
+ * Accuracy: the residual form meets the GEMM bound with ref = sum_k A B + bias + residual; the
+ * GELU form satisfies |c - gelu(ref)| <= 2^-7 |gelu(ref)| + 2^-19 sum_k |A B| + 2^-126 with
+ * ref = sum_k A B + bias (GELU's slope is at most 1.129).  Operands, formats, errors and the
+ * other rules as for the plain entry points of the same kind.  Batched: residual +
+ * i*stride_residual (bf16 elements; 0 reuses one residual for every batch).
+ * ------------------------------------------------------------------------------------------- */
+int mx_gemm_fp8_fp4_bias_residual(const void* a, const void* a_scale, const void* b,
+                                  const void* b_scale, const void* bias, const void* residual,
+                                  void* c, int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp8_fp4_bias_residual_strided_batched(const void* a, const void* a_scale,
+                                                  const void* b, const void* b_scale,
+                                                  const void* bias, const void* residual, void* c,
+                                                  int64_t M, int64_t N, int64_t K, int64_t batch,
+                                                  int64_t stride_a, int64_t stride_a_scale,
+                                                  int64_t stride_b, int64_t stride_b_scale,
+                                                  int64_t stride_bias, int64_t stride_residual,
+                                                  int64_t stride_c, void* stream);
+int mx_gemm_fp8_fp4_bias_gelu(const void* a, const void* a_scale, const void* b,
+                              const void* b_scale, const void* bias, void* c, int64_t M, int64_t N,
+                              int64_t K, void* stream);
+int mx_gemm_fp8_fp4_bias_gelu_strided_batched(const void* a, const void* a_scale, const void* b,
+                                              const void* b_scale, const void* bias, void* c,
+                                              int64_t M, int64_t N, int64_t K, int64_t batch,
+                                              int64_t stride_a, int64_t stride_a_scale,
+                                              int64_t stride_b, int64_t stride_b_scale,
+                                              int64_t stride_bias, int64_t stride_c, void* stream);
+
+int mx_gemm_fp8_fp8_bias_residual(const void* a, const void* a_scale, const void* b,
+                                  const void* b_scale, const void* bias, const void* residual,
+                                  void* c, int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp8_fp8_bias_residual_strided_batched(const void* a, const void* a_scale,
+                                                  const void* b, const void* b_scale,
+                                                  const void* bias, const void* residual, void* c,
+                                                  int64_t M, int64_t N, int64_t K, int64_t batch,
+                                                  int64_t stride_a, int64_t stride_a_scale,
+                                                  int64_t stride_b, int64_t stride_b_scale,
+                                                  int64_t stride_bias, int64_t stride_residual,
+                                                  int64_t stride_c, void* stream);
+int mx_gemm_fp8_fp8_bias_gelu(const void* a, const void* a_scale, const void* b,
+                              const void* b_scale, const void* bias, void* c, int64_t M, int64_t N,
+                              int64_t K, void* stream);
+int mx_gemm_fp8_fp8_bias_gelu_strided_batched(const void* a, const void* a_scale, const void* b,
+                                              const void* b_scale, const void* bias, void* c,
+                                              int64_t M, int64_t N, int64_t K, int64_t batch,
+                                              int64_t stride_a, int64_t stride_a_scale,
+                                              int64_t stride_b, int64_t stride_b_scale,
+                                              int64_t stride_bias, int64_t stride_c, void* stream);
+
+int mx_gemm_fp4_fp4_bias_residual(const void* a, const void* a_scale, const void* b,
+                                  const void* b_scale, const void* bias, const void* residual,
+                                  void* c, int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp4_fp4_bias_residual_strided_batched(const void* a, const void* a_scale,
+                                                  const void* b, const void* b_scale,
+                                                  const void* bias, const void* residual, void* c,
+                                                  int64_t M, int64_t N, int64_t K, int64_t batch,
+                                                  int64_t stride_a, int64_t stride_a_scale,
+                                                  int64_t stride_b, int64_t stride_b_scale,
+                                                  int64_t stride_bias, int64_t stride_residual,
+                                                  int64_t stride_c, void* stream);
+int mx_gemm_fp4_fp4_bias_gelu(const void* a, const void* a_scale, const void* b,
+                              const void* b_scale, const void* bias, void* c, int64_t M, int64_t N,
+                              int64_t K, void* stream);
+int mx_gemm_fp4_fp4_bias_gelu_strided_batched(const void* a, const void* a_scale, const void* b,
+                                              const void* b_scale, const void* bias, void* c,
+                                              int64_t M, int64_t N, int64_t K, int64_t batch,
+                                              int64_t stride_a, int64_t stride_a_scale,
+                                              int64_t stride_b, int64_t stride_b_scale,
+                                              int64_t stride_bias, int64_t stride_c, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,8 @@ Everything here is written to be read against the pages it follows, not to be fa
 * "AstrAI commit log" page: the fused-bias commit (bias added in fp32 before the single bf16
   rounding of the GEMM output).
 * "fp4-gemm README" page: the epilogue that emits the next projection's quantized input (O4: the
-  bf16 GEMM output quantized with act_quant).
+  bf16 GEMM output quantized with act_quant), the MXFP4 operand produced from activations (O5)
+  and the bias + residual and bias + GELU epilogues (O6).
 
 Decoded values and the GEMM are carried in float64: every decoded value has at most 4
 significant bits times a power of two, so every product of two of them is exact in float64, and
@@ -29,6 +30,9 @@ Readings taken where the pages are silent (each is listed in the design notes as
 * The GEMM reference is the unrounded float64 value  sum_k a*b + bias ; the bf16 output is
   accepted when |out - ref| <= 2^-7 |ref| + 2^-20 sum_k |a*b|.
 * Non-finite activations, NaN E4M3 codes (0x7F, 0xFF) and the NaN scale byte 255 are refused.
+* The MXFP4 producer uses act_quant's rule with E2M1's largest magnitude 6 (O5).
+* The residual is added before the single bf16 rounding, like the bias; GELU is the exact
+  x * Phi(x) of (sum + bias) (O6).
 
 No function here is "parity unpinned" except the GEMM below the stated tolerance (the bf16 output
 of any correct implementation may differ from another's inside that bound); the quantized GEMM

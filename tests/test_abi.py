@@ -35,8 +35,12 @@ def test_header_declares_the_full_boundary():
     for k in ("fp8_fp4", "fp8_fp8"):
         for v in ("_quant", "_quant_strided_batched"):
             assert f"mx_gemm_{k}{v}" in names
+    for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
+        for v in ("_bias_residual", "_bias_residual_strided_batched", "_bias_gelu",
+                  "_bias_gelu_strided_batched"):
+            assert f"mx_gemm_{k}{v}" in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 22
+    assert len(names) == 34
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -160,6 +164,40 @@ def test_gemm_quant_argument_errors(lib, kind):
     assert gs(*ok, 2, 1024, 32, 4096, 128, 0, 1024, 0, None) == mx.MX_ERR_STRIDE  # q_s stride 0
     assert gs(*ok, 2, 1024, 32, 4096, 128, 0, 1032, 32, None) == mx.MX_ERR_ALIGN  # q batch
     assert gs(*ok, 2, 1024, 32, 4096, 128, -1, 1024, 32, None) == mx.MX_ERR_STRIDE
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+def test_gemm_epilogue_argument_errors(lib, kind):
+    gr = getattr(lib, f"mx_gemm_{kind}_bias_residual")
+    grs = getattr(lib, f"mx_gemm_{kind}_bias_residual_strided_batched")
+    gg = getattr(lib, f"mx_gemm_{kind}_bias_gelu")
+    ggs = getattr(lib, f"mx_gemm_{kind}_bias_gelu_strided_batched")
+    # a, a_s, b, b_s, bias (may be NULL), residual, c, M, N, K
+    ok = (A16, A16, A16, A16, None, A16, A16, 16, 64, 64)
+    assert gr(*ok[:5], None, *ok[6:], None) == mx.MX_ERR_NULL        # residual
+    assert gr(*ok[:6], None, *ok[7:], None) == mx.MX_ERR_NULL        # c
+    assert gr(*ok[:7], 16, 64, 40, None) == mx.MX_ERR_SHAPE          # K not a multiple of 32
+    assert gr(None, None, None, None, None, None, None, 16, 0, 64, None) == mx.MX_OK   # empty
+    # batch, sa, sas, sb, sbs, sbias, sres, sc
+    assert grs(*ok, 2, 1024, 32, 4096, 128, 0, -1, 1024, None) == mx.MX_ERR_STRIDE
+    assert grs(*ok, 2, 1024, 32, 4096, 128, 0, 1024, 0, None) == mx.MX_ERR_STRIDE   # c stride 0
+    assert grs(*ok, 2, 1024, 32, 4096, 128, 0, 0, 1024, None) != mx.MX_ERR_STRIDE   # broadcast
+    og = (A16, A16, A16, A16, None, A16, 16, 64, 64)
+    assert gg(*og[:5], None, *og[6:], None) == mx.MX_ERR_NULL        # c
+    assert gg(*og[:6], 16, 64, 0, None) == mx.MX_ERR_SHAPE
+    assert ggs(*og, 2, 1024, 32, 4096, 128, 0, 0, None) == mx.MX_ERR_STRIDE
+    assert ggs(*og, 2, 1032, 32, 4096, 128, 0, 1024, None) == mx.MX_ERR_ALIGN
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+def test_gemm_epilogue_valid_args_without_gpu_report_device(lib, kind):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    gr = getattr(lib, f"mx_gemm_{kind}_bias_residual")
+    gg = getattr(lib, f"mx_gemm_{kind}_bias_gelu")
+    assert gr(A16, A16, A16, A16, None, A16, A16, 16, 64, 64, None) == mx.MX_ERR_DEVICE
+    assert gg(A16, A16, A16, A16, A16, A16, 16, 64, 64, None) == mx.MX_ERR_DEVICE
 
 
 @pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8"])
