@@ -235,6 +235,35 @@ def main():
                  "bias_gelu_tflops": round(flops / (gelu_ms * 1e-3) / 1e12, 2)}
     del res_t
 
+    # ---- split-K on the down-projection shape 4096x2048x7168 (128 output tiles of 256x256 for
+    # 256 CUs): the same inputs through the plain and the split-K entry point
+    wd = synth.gemm_inputs("fp8", "fp4", 4096, 2048, 7168, 1006, with_bias=True,
+                           name="fp8xmxfp4_m4096_n2048_k7168_bias")
+    ad, asd, bd, bsd = dev_u8(wd.a), dev_u8(wd.a_s), dev_u8(wd.b), dev_u8(wd.b_s)
+    biasd = dev_bf16(wd.bias)
+    cd = torch.empty((wd.M, wd.N), dtype=torch.bfloat16, device="cuda")
+    wsd = torch.zeros(mx.mx_gemm_splitk_workspace_size(wd.M, wd.N, wd.K), dtype=torch.uint8,
+                      device="cuda")
+
+    def down_plain():
+        mx.mx_gemm_fp8_fp4(ad, asd, bd, bsd, cd, bias=biasd, stream=stream)
+
+    def down_split():
+        mx.mx_gemm_fp8_fp4_splitk(ad, asd, bd, bsd, cd, wsd, bias=biasd, stream=stream)
+
+    for _ in range(200):
+        down_plain()
+        down_split()
+    dflops = 2.0 * wd.M * wd.N * wd.K
+    plain_ms = time_events(down_plain, 50, torch)
+    split_ms = time_events(down_split, 50, torch)
+    splitk = {"workload": "FP8xMXFP4 GEMM 4096x2048x7168 + bias (128 tiles of 256x256): plain "
+                          "launch (128x128 tiles) against K split in two",
+              "plain_ms": round(plain_ms, 5), "plain_tflops": round(dflops / (plain_ms * 1e-3) / 1e12, 2),
+              "splitk_ms": round(split_ms, 5), "splitk_tflops": round(dflops / (split_ms * 1e-3) / 1e12, 2),
+              "speedup": round(plain_ms / split_ms, 3), "workspace_bytes": int(wsd.numel())}
+    del ad, asd, bd, bsd, biasd, cd, wsd
+
     # ---- standalone act_quant on [16384, 7168], sustained: back-to-back launches rotating over
     # three input/output sets (1.07 GB, far beyond the 256 MB last-level cache), so each launch
     # reads its input from HBM and pays for the previous launch's write-back.
@@ -313,6 +342,7 @@ def main():
            "gemm_only_tflops": round(gemm_tflops, 2)}
     out["next_layer_quant"] = next_layer
     out["epilogues"] = epilogues
+    out["splitk"] = splitk
     if others is not None:
         out["other_configs"] = others
     if not args.no_cpu:

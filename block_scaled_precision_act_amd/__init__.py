@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmx_gfx950.so")
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_STRIDE, MX_ERR_DEVICE, MX_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5, -6
+MX_ERR_WORKSPACE = -7
 
 _lib = None
 
@@ -54,6 +55,8 @@ for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
     _SIGS[f"mx_gemm_{_n}_bias_gelu"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_bias_gelu_strided_batched"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                                         _I, _I, _I, _I, _I, _I, _P]
+    _SIGS[f"mx_gemm_{_n}_splitk"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]
+_SIGS["mx_gemm_splitk_workspace_size"] = [_I, _I, _I]
 for _n in ("fp8_fp4", "fp8_fp8"):
     _SIGS[f"mx_gemm_{_n}_quant"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_quant_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -75,6 +78,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.mx_status_str.argtypes = [ctypes.c_int]
     lib.mx_status_str.restype = ctypes.c_char_p
+    lib.mx_gemm_splitk_workspace_size.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -269,3 +273,35 @@ def mx_gemm_fp8_fp8_bias_gelu(a, a_s, b, b_s, c, bias=None, stream=None):
 def mx_gemm_fp4_fp4_bias_gelu(a, a_s, b, b_s, c, bias=None, stream=None):
     """As mx_gemm_fp8_fp4_bias_gelu for MXFP4 activations."""
     _gemm_epilogue("fp4_fp4", "gelu", a, a_s, b, b_s, c, bias, None, stream)
+
+
+def mx_gemm_splitk_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace the _splitk entry points need for an M x N x K problem (0: not split)."""
+    return int(load().mx_gemm_splitk_workspace_size(M, N, K))
+
+
+def _gemm_splitk(kind: str, a, a_s, b, b_s, c, workspace, bias=None, stream=None):
+    M, N = c.shape
+    K = a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    name = f"mx_gemm_{kind}_splitk"
+    _check(name, getattr(load(), name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias),
+                                       _ptr(c), M, N, K, _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
+
+
+def mx_gemm_fp8_fp4_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4 (single problem) with K split across workgroups when the shape has few
+    output tiles; workspace: a zero-filled device buffer of mx_gemm_splitk_workspace_size bytes
+    (256-byte aligned; left reusable), or None for shapes that are not split."""
+    _gemm_splitk("fp8_fp4", a, a_s, b, b_s, c, workspace, bias, stream)
+
+
+def mx_gemm_fp8_fp8_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_splitk for FP8 weights."""
+    _gemm_splitk("fp8_fp8", a, a_s, b, b_s, c, workspace, bias, stream)
+
+
+def mx_gemm_fp4_fp4_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_splitk for MXFP4 activations."""
+    _gemm_splitk("fp4_fp4", a, a_s, b, b_s, c, workspace, bias, stream)

@@ -46,6 +46,8 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 template <int V>
 struct IntC { static constexpr int value = V; };
@@ -79,6 +81,11 @@ struct Args {
   int64_t stride_q, stride_qs;
   const uint16_t* res;
   int64_t stride_res;
+  // SPLIT: K split into `splits` equal ranges of K steps per tile; fp32 partial tiles in `ws`
+  // (tile-major, then range), one arrival counter per tile in `counters` (zero between calls).
+  float* ws;
+  uint32_t* counters;
+  int splits;
 };
 
 // fp32 value of an E8M0 byte (2^(b-127)); byte 0 is the fp32 subnormal 2^-127.
@@ -438,7 +445,11 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
 // EPI (bf16 output only): kEpiResidual adds the bf16 residual [M, N] before the rounding,
 // kEpiGelu applies GELU to (sum + bias); both take the bias pointer as optional (BIAS is true
 // for them and a null bias adds nothing).
-template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN>
+// SPLIT (splits == 2): workgroup b computes K range (b % 2) of tile b / 2 and stores its fp32
+// partial tile; the workgroup that arrives second at the tile's counter (no workgroup ever waits
+// for another) adds the other partial to its own and runs the epilogue.
+template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT, int BM, int BN, int WM,
+          int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;     // WM x WN wavefronts
@@ -455,8 +466,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   const int l32 = lane & 31;
   const int wm = wave / WN, wn = wave % WN;
 
+  int tile_id = blockIdx.x, ntiles = gridDim.x, split = 0;
+  if constexpr (SPLIT) {
+    split = blockIdx.x % p.splits;
+    tile_id = blockIdx.x / p.splits;
+    ntiles = gridDim.x / p.splits;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  tile_of(tile_id, ntiles, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t bz = blockIdx.y;
   const int m0 = tm * BM, n0 = tn * BN;
 
@@ -486,19 +503,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   bf16x8 fa[2][TM], fb[2][TN];
 
   // Pipeline: step k's codes are staged into LDS stage k & 1 during step k-1, piece by piece, and
-  // each piece is reloaded for step k+1 right after it is staged.
-  const int KT = (p.K + kBK - 1) / kBK;
-  const int last_partial = (p.K % kBK) != 0 ? KT - 1 : -1;
-  sa.load_all(0, last_partial == 0);
-  sb.load_all(0, last_partial == 0);
-  br.load_scales(0);
+  // each piece is reloaded for step k+1 right after it is staged.  Steps [k0, k0 + KT) of the
+  // KT_all steps of K (all of them unless SPLIT); loads take absolute step indices.
+  const int KT_all = (p.K + kBK - 1) / kBK;
+  int k0 = 0, KT = KT_all;
+  if constexpr (SPLIT) {
+    k0 = static_cast<int>(static_cast<int64_t>(split) * KT_all / p.splits);
+    KT = static_cast<int>(static_cast<int64_t>(split + 1) * KT_all / p.splits) - k0;
+  }
+  const int last_partial = (p.K % kBK) != 0 ? KT_all - 1 : -1;
+  sa.load_all(k0, last_partial == k0);
+  sb.load_all(k0, last_partial == k0);
+  br.load_scales(k0);
   sa.store_all(lds);
   sb.store_all(lds);
   if (KT > 1) {
     static_for<0, kParts>([&](auto pc) {
       constexpr int P = decltype(pc)::value;
-      sa.template load_part<P>(1, last_partial == 1);
-      sb.template load_part<P>(1, last_partial == 1);
+      sa.template load_part<P>(k0 + 1, last_partial == k0 + 1);
+      sb.template load_part<P>(k0 + 1, last_partial == k0 + 1);
     });
   }
   __syncthreads();
@@ -506,13 +529,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   read_a<TM>(lds, a_base, coff[0], fa[0]);
   br.read_raw_all(lds);
   br.template decode_all<0>(fb[0]);
-  if (KT > 1) br.load_scales(1);
+  if (KT > 1) br.load_scales(k0 + 1);
 
   int kt = 0;
   for (; kt + 2 < KT; ++kt) {
     k_step<true, true>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes, a_base,
-                       coff, sa, sb, br, fa, fb, acc, kt + 2, kt + 2 == last_partial);
-    br.load_scales(kt + 2);
+                       coff, sa, sb, br, fa, fb, acc, k0 + kt + 2, k0 + kt + 2 == last_partial);
+    br.load_scales(k0 + kt + 2);
   }
   if (kt + 1 < KT) {
     k_step<true, false>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes, a_base,
@@ -521,6 +544,68 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
   k_step<false, false>(lds + (kt & 1) * kStageBytes, lds, a_base, coff, sa, sb, br, fa, fb, acc,
                        0, false);
+
+  if constexpr (SPLIT) {
+    // This range's partial tile: thread t's accumulator values as 16-byte units u at
+    // (u * NT + t), so every store and load below is one coalesced 1 KB row per wavefront.
+    // The partials are stored and loaded with device-scope cache policy (sc1): written through
+    // to the memory every XCD shares instead of sitting dirty in this XCD's L2, so the release
+    // below has little to write back.
+    constexpr int kUnits = TM * TN * 4;
+    constexpr uint32_t kTileBytes = static_cast<uint32_t>(kUnits) * NT * 16;
+    constexpr int kDeviceScope = 16;     // the sc1 cache-policy bit
+    const __amdgpu_buffer_rsrc_t wsr = make_rsrc(
+        reinterpret_cast<const uint8_t*>(p.ws) + static_cast<int64_t>(tile_id) * p.splits * kTileBytes,
+        kTileBytes * static_cast<uint32_t>(p.splits));
+    const uint32_t lane_off = threadIdx.x * 16u;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t off = static_cast<uint32_t>(((i * TN + j) * 4 + q) * NT * 16) + lane_off;
+          const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                         acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), wsr, off,
+                                                 split * kTileBytes, kDeviceScope);
+        }
+    // The barrier orders every wavefront's partial stores before thread 0's device-scope
+    // acquire-release increment: its release writes this XCD's L2 back, so the partial reaches
+    // the memory every XCD shares; its acquire (on the last workgroup) invalidates this CU's and
+    // XCD's caches, so the loads below, ordered after it by the second barrier, see the other
+    // ranges' partials.  One such fence pair per workgroup: a device-scope fence writes back or
+    // invalidates a whole L2, far too costly to run in every wavefront.
+    __shared__ uint32_t arrived;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t before = __hip_atomic_fetch_add(p.counters + tile_id, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+      // the last arrival leaves the counter at zero for the next call
+      if (before == static_cast<uint32_t>(p.splits - 1))
+        __hip_atomic_store(p.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      arrived = before;
+    }
+    __syncthreads();
+    if (arrived != static_cast<uint32_t>(p.splits - 1)) return;   // not the last: done
+    // Two ranges: the tile is own + other, and fp32 addition is commutative, so the sum is the
+    // same bits whichever workgroup arrives last.
+    const int other = 1 - split;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t off = static_cast<uint32_t>(((i * TN + j) * 4 + q) * NT * 16) + lane_off;
+          const v4f v = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    wsr, off, other * kTileBytes, kDeviceScope));
+          acc[i][j][4 * q] += v[0];
+          acc[i][j][4 * q + 1] += v[1];
+          acc[i][j][4 * q + 2] += v[2];
+          acc[i][j][4 * q + 3] += v[3];
+        }
+  }
 
   // Epilogue, staged through LDS: fp32 + bias, one bf16 rounding, written into a row-major bf16
   // tile [BM][BN] (16-byte chunk c of row r at chunk c ^ (4 * bit 2 of r): the two row groups a
@@ -636,11 +721,12 @@ constexpr int lds_bytes() {
   return stages > tile ? stages : tile;
 }
 
-template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN>
+template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN,
+          bool SPLIT = false>
 hipError_t launch_kernel(const Args& p, dim3 grid, hipStream_t stream) {
   constexpr int kLds = lds_bytes<AF, BF, BM, BN>();
-  static_assert(kLds <= 160 * 1024, "LDS");
-  auto k = gemm_bf16_kernel<AF, BF, BIAS, QUANT, EPI, BM, BN, WM, WN>;
+  static_assert(kLds + 16 <= 160 * 1024, "LDS");
+  auto k = gemm_bf16_kernel<AF, BF, BIAS, QUANT, EPI, SPLIT, BM, BN, WM, WN>;
   // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
   static const hipError_t attr_ok = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
@@ -654,7 +740,8 @@ hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
-         g.q, g.qs, g.stride_q, g.stride_qs, g.residual, g.stride_res};
+         g.q, g.qs, g.stride_q, g.stride_qs, g.residual, g.stride_res,
+         nullptr, nullptr, 1};
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
   if constexpr (AF == kFp8) {
     if (g.q) {
@@ -670,8 +757,30 @@ hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
                 : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN>(p, grid, stream);
 }
 
+// Split-K launch: 256x256 tiles, grid = tiles * splits (one batch), bf16 output with an optional
+// bias.  The workspace holds the tile counters (zero on entry, left zero on exit) and then the
+// fp32 partial tiles.
+template <int AF, int BF>
+hipError_t launch_split(const GemmProblem& g, const SplitPlan& plan, hipStream_t stream) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+  uint8_t* ws = static_cast<uint8_t*>(g.workspace);
+  Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
+         (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
+         g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
+         nullptr, nullptr, 0, 0, nullptr, 0,
+         reinterpret_cast<float*>(ws + plan.counter_bytes), reinterpret_cast<uint32_t*>(ws),
+         plan.splits};
+  dim3 grid(p.tiles_m * p.tiles_n * plan.splits, 1);
+  return g.bias ? launch_kernel<AF, BF, true, false, kEpiPlain, BM, BN, WM, WN, true>(p, grid, stream)
+                : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN, true>(p, grid, stream);
+}
+
 template <int AF, int BF>
 hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream_t stream) {
+  if (g.workspace) {
+    const SplitPlan plan = plan_split(g.M, g.N, g.K, g.batch);
+    if (plan.splits > 1) return launch_split<AF, BF>(g, plan, stream);
+  }
   // Largest tile that still gives every CU a workgroup; the smallest one otherwise.
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   auto tiles = [&](int bm, int bn) {
@@ -680,7 +789,9 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   // A last partial wave of 256x256 tiles is not worth splitting further: on 4096x7168 (448 tiles,
   // 1.75 waves) the 192 tiles of the second wave run 18% faster per CU than a full wave does, and
   // finishing them as 256 tiles of 256x192 in a second launch measured the same total time.
-  if (tiles(256, 256) >= cus) return launch_tile<AF, BF, 256, 256, 2, 4>(g, stream);
+  // Above half the CUs, one wave of 256x256 tiles beats the three or four waves of 128x128 tiles
+  // the same output needs (a 128x128 step costs 0.37 of a 256x256 step for a quarter of the work).
+  if (2 * tiles(256, 256) > cus) return launch_tile<AF, BF, 256, 256, 2, 4>(g, stream);
   if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, stream);
   return launch_tile<AF, BF, 64, 64, 2, 2>(g, stream);
 }

@@ -117,6 +117,10 @@ struct GemmCall {
   int epi = mx::kEpiPlain;
   const void* res = nullptr;
   int64_t sres = 0;
+  // Split-K workspace (the _splitk entry points).
+  bool splitk = false;
+  void* ws = nullptr;
+  int64_t ws_bytes = 0;
 };
 
 int validate_gemm(const GemmCall& g) {
@@ -134,6 +138,12 @@ int validate_gemm(const GemmCall& g) {
   if (!g.a || !g.a_s || !g.b || !g.b_s) return MX_ERR_NULL;
   if (g.quant ? (!g.q || !g.qs) : !g.c) return MX_ERR_NULL;
   if (g.needs_bias && !g.bias) return MX_ERR_NULL;
+  if (g.splitk) {
+    const mx::SplitPlan plan = mx::plan_split(g.M, g.N, g.K, g.batch);
+    if (plan.splits > 1 && (!g.ws || g.ws_bytes < plan.bytes ||
+                            (reinterpret_cast<uintptr_t>(g.ws) & 255u) != 0))
+      return MX_ERR_WORKSPACE;
+  }
   if (g.epi == mx::kEpiResidual && !g.res) return MX_ERR_NULL;
   if (!mx::aligned16(g.a) || !mx::aligned16(g.b)) return MX_ERR_ALIGN;
   if (g.sa % 16 != 0 || g.sb % 16 != 0) return MX_ERR_ALIGN;
@@ -166,6 +176,7 @@ int gemm_impl(const GemmCall& g, void* stream) {
   p.epi = g.epi;
   p.residual = static_cast<const uint16_t*>(g.res);
   p.stride_res = g.sres;
+  if (g.splitk) p.workspace = g.ws;
   if (g.quant) {
     p.c = nullptr;
     p.q = static_cast<uint8_t*>(g.q);
@@ -188,6 +199,13 @@ GemmCall batched(int af, int bf, const void* a, const void* a_s, const void* b, 
                  bool needs_bias) {
   return GemmCall{af, bf, a, a_s, b, b_s, bias, c, M, N, K, batch,
                   sa, sas, sb, sbs, sbias, sc, needs_bias};
+}
+
+GemmCall with_workspace(GemmCall g, void* ws, int64_t ws_bytes) {
+  g.splitk = true;
+  g.ws = ws;
+  g.ws_bytes = ws_bytes;
+  return g;
 }
 
 GemmCall with_epilogue(GemmCall g, int epi, const void* res, int64_t sres) {
@@ -252,6 +270,7 @@ const char* mx_status_str(int status) {
     case MX_ERR_STRIDE: return "invalid stride (negative, or output stride 0 with batch > 1)";
     case MX_ERR_DEVICE: return "no gfx950 device is current";
     case MX_ERR_LAUNCH: return "kernel launch failed";
+    case MX_ERR_WORKSPACE: return "split-K workspace missing, too small or not 256-byte aligned";
     default: return "unknown status";
   }
 }
@@ -367,6 +386,26 @@ MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
                                    mx::kEpiGelu, nullptr, 0),                                 \
                      stream);                                                                 \
   }
+
+int64_t mx_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (check_k(K) != MX_OK || M < 0 || N < 0) return 0;
+  return mx::plan_split(M, N, K, 1).bytes;
+}
+
+#define MX_GEMM_SPLITK_ENTRY_POINT(NAME, AF, BF)                                              \
+  int mx_gemm_##NAME##_splitk(const void* a, const void* a_s, const void* b, const void* b_s, \
+                              const void* bias, void* c, int64_t M, int64_t N, int64_t K,     \
+                              void* workspace, int64_t workspace_bytes, void* stream) {       \
+    return gemm_impl(with_workspace(single(AF, BF, a, a_s, b, b_s, bias, c, M, N, K, false),  \
+                                    workspace, workspace_bytes),                              \
+                     stream);                                                                 \
+  }
+
+MX_GEMM_SPLITK_ENTRY_POINT(fp8_fp4, mx::kFp8, mx::kFp4)
+MX_GEMM_SPLITK_ENTRY_POINT(fp8_fp8, mx::kFp8, mx::kFp8)
+MX_GEMM_SPLITK_ENTRY_POINT(fp4_fp4, mx::kFp4, mx::kFp4)
+
+#undef MX_GEMM_SPLITK_ENTRY_POINT
 
 MX_GEMM_EPILOGUE_ENTRY_POINTS(fp8_fp4, mx::kFp8, mx::kFp4)
 MX_GEMM_EPILOGUE_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)

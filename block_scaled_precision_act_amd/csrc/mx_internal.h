@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <cstdint>
 
 namespace mx {
@@ -33,7 +34,40 @@ struct GemmProblem {
   int epi = kEpiPlain;    // kEpiResidual / kEpiGelu: bf16 output only (q == nullptr)
   const uint16_t* residual = nullptr;   // kEpiResidual: bf16 [M, N], may be c itself
   int64_t stride_res = 0;
+  void* workspace = nullptr;            // split-K workspace (plan_split), or nullptr: no split
 };
+
+// Split-K plan of the tiled kernel for problems with fewer 256x256 output tiles than the 256 CUs
+// of an MI355X and a long K (large down-projections): K is cut into two equal ranges of 64-wide
+// steps, each range of each tile is one workgroup, and the second workgroup to finish a tile
+// adds the other's fp32 partial tile to its own.  Only single problems (batch 1) with 65..128
+// tiles (where the unsplit launch needs two or more waves of 128x128 tiles) and at least 40 steps
+// per range: elsewhere the partial tiles' traffic (256 KB written and read per tile, through one
+// CU) cost more than the idle CUs did (measured).  The plan depends on the shape alone, so the workspace size a caller
+// asks for is the one the launch uses.  Workspace: `counter_bytes` of per-tile counters (zero
+// between calls), then tiles * 2 partial tiles of 256 * 256 fp32.
+struct SplitPlan {
+  int splits = 1;
+  int64_t counter_bytes = 0;
+  int64_t bytes = 0;
+};
+constexpr int64_t kSplitTargetCUs = 256;
+constexpr int64_t kMinSplitTiles = 65;
+constexpr int64_t kMinStepsPerSplit = 40;
+
+inline SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  SplitPlan p;
+  if (batch != 1 || M <= 0 || N <= 0 || K <= 0) return p;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t steps = (K + 63) / 64;
+  if (2 * tiles > kSplitTargetCUs || tiles < kMinSplitTiles || steps < 2 * kMinStepsPerSplit)
+    return p;
+  const int64_t s = 2;
+  p.splits = static_cast<int>(s);
+  p.counter_bytes = (tiles * 4 + 255) / 256 * 256;
+  p.bytes = p.counter_bytes + tiles * s * 256 * 256 * 4;
+  return p;
+}
 
 struct DeviceInfo {
   int device;

@@ -49,7 +49,8 @@ enum {
   MX_ERR_ALIGN = -3,   /* an operand base or batch stride breaks 16-byte alignment           */
   MX_ERR_STRIDE = -4,  /* negative stride, or output stride 0 with batch > 1                 */
   MX_ERR_DEVICE = -5,  /* no HIP device, or the current device is not gfx950                 */
-  MX_ERR_LAUNCH = -6   /* the kernel launch itself failed                                    */
+  MX_ERR_LAUNCH = -6,  /* the kernel launch itself failed                                    */
+  MX_ERR_WORKSPACE = -7 /* split-K workspace NULL, smaller than asked or not 256-B aligned    */
 };
 
 typedef struct mx_caps {
@@ -302,6 +303,42 @@ int mx_gemm_fp4_fp4_bias_gelu_strided_batched(const void* a, const void* a_scale
                                               int64_t stride_a, int64_t stride_a_scale,
                                               int64_t stride_b, int64_t stride_b_scale,
                                               int64_t stride_bias, int64_t stride_c, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Split-K GEMM for shapes with few output tiles and a long K (large down-projections).
+ *
+ * The "fp4-gemm README" page offers stream-K variants of its GEMM, selected only for validated
+ * large down-projection shapes (API list; the paragraph after the schedule variants).  Here the
+ * load-balancing variant splits K: when an M x N problem has fewer 256 x 256 output tiles than
+ * the 256 CUs of an MI355X, each tile's K is cut into 2..4 equal ranges (at least 16 steps of 64
+ * each) computed by separate workgroups; each stores its fp32 partial tile in the workspace, and
+ * the workgroup that finishes a tile last adds the partials in range order (the same order on
+ * every run, so results are reproducible), adds the bias and rounds once to bf16.  No workgroup
+ * waits for another.  Shapes the plan does not split run exactly as mx_gemm_<kind>_bias (or
+ * without bias) do, and need no workspace.
+ *
+ * mx_gemm_splitk_workspace_size: bytes of workspace an M x N x K call needs; 0 when that shape is
+ *   not split (also for invalid sizes).  It depends on the shape alone (safe without a GPU).
+ * mx_gemm_<kind>_splitk: as mx_gemm_<kind>_bias with bias optional (NULL: no bias), single
+ *   problem, plus
+ *   workspace        device memory of at least the size above, 256-byte aligned; before its
+ *                    first use it must be zero-filled (its head holds per-tile counters); every
+ *                    completed call leaves those counters zero again, so it can be reused as is.
+ *                    Calls sharing one workspace must not run concurrently.
+ *   workspace_bytes  its size.  MX_ERR_WORKSPACE when a split shape gets a NULL, smaller or
+ *                    misaligned workspace.
+ * Accuracy: the bound of the plain GEMM (the partial sums are fp32, added in fp32).
+ * ------------------------------------------------------------------------------------------- */
+int64_t mx_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K);
+int mx_gemm_fp8_fp4_splitk(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                           const void* bias, void* c, int64_t M, int64_t N, int64_t K,
+                           void* workspace, int64_t workspace_bytes, void* stream);
+int mx_gemm_fp8_fp8_splitk(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                           const void* bias, void* c, int64_t M, int64_t N, int64_t K,
+                           void* workspace, int64_t workspace_bytes, void* stream);
+int mx_gemm_fp4_fp4_splitk(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                           const void* bias, void* c, int64_t M, int64_t N, int64_t K,
+                           void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

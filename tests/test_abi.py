@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "mx.h")
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mx_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(mx_\w+)\s*\(", src, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -39,8 +39,11 @@ def test_header_declares_the_full_boundary():
         for v in ("_bias_residual", "_bias_residual_strided_batched", "_bias_gelu",
                   "_bias_gelu_strided_batched"):
             assert f"mx_gemm_{k}{v}" in names
+    for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
+        assert f"mx_gemm_{k}_splitk" in names
+    assert "mx_gemm_splitk_workspace_size" in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 34
+    assert len(names) == 38
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -56,7 +59,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    for st in range(0, -7, -1):
+    for st in range(0, -8, -1):
         s = mx.status_str(st)
         assert s and s != "unknown status"
     assert mx.status_str(-99) == "unknown status"
@@ -187,6 +190,40 @@ def test_gemm_epilogue_argument_errors(lib, kind):
     assert gg(*og[:6], 16, 64, 0, None) == mx.MX_ERR_SHAPE
     assert ggs(*og, 2, 1024, 32, 4096, 128, 0, 0, None) == mx.MX_ERR_STRIDE
     assert ggs(*og, 2, 1032, 32, 4096, 128, 0, 1024, None) == mx.MX_ERR_ALIGN
+
+
+def test_splitk_workspace_size_plan():
+    # 256x256 tiles; two K ranges when there are 65..128 tiles and >= 80 K steps of 64;
+    # workspace = per-tile counters (rounded up to 256 B) + tiles * 2 fp32 tiles.
+    def size(tiles):
+        return ((tiles * 4 + 255) // 256) * 256 + tiles * 2 * 256 * 256 * 4
+    assert mx.mx_gemm_splitk_workspace_size(4096, 2048, 7168) == size(128)
+    assert mx.mx_gemm_splitk_workspace_size(2000, 4000, 5152) == size(128)
+    assert mx.mx_gemm_splitk_workspace_size(1280, 3328, 5120) == size(65)
+    assert mx.mx_gemm_splitk_workspace_size(1280, 3328, 5056) == 0        # 79 K steps
+    assert mx.mx_gemm_splitk_workspace_size(2048, 2048, 8192) == 0        # 64 tiles
+    assert mx.mx_gemm_splitk_workspace_size(4096, 2304, 8192) == 0        # 144 tiles
+    assert mx.mx_gemm_splitk_workspace_size(4096, 7168, 2048) == 0        # 448 tiles
+    assert mx.mx_gemm_splitk_workspace_size(64, 64, 48) == 0              # invalid K
+    assert mx.mx_gemm_splitk_workspace_size(-1, 64, 2048) == 0
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+def test_gemm_splitk_argument_errors(lib, kind):
+    g = getattr(lib, f"mx_gemm_{kind}_splitk")
+    need = mx.mx_gemm_splitk_workspace_size(4096, 2048, 7168)
+    # a, a_s, b, b_s, bias, c, M, N, K, workspace, workspace_bytes
+    base = (A16, A16, A16, A16, None, A16, 4096, 2048, 7168)
+    assert g(*base, None, 0, None) == mx.MX_ERR_WORKSPACE
+    assert g(*base, A16, need - 1, None) == mx.MX_ERR_WORKSPACE
+    assert g(*base, A16 + 16, need, None) == mx.MX_ERR_WORKSPACE          # not 256-B aligned
+    assert g(A16, A16, A16, A16, None, None, 4096, 2048, 7168, A16, need, None) == mx.MX_ERR_NULL
+    assert g(*base[:8], 7000, A16, need, None) == mx.MX_ERR_SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert g(*base, A16, need, None) == mx.MX_ERR_DEVICE
+        # a shape that is not split needs no workspace
+        assert g(A16, A16, A16, A16, None, A16, 4096, 7168, 2048, None, 0, None) == mx.MX_ERR_DEVICE
 
 
 @pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])

@@ -1,0 +1,151 @@
+"""Split-K GEMM on the GPU against the oracle.
+
+Every output must meet the GEMM bound against the exact float64 result.  The split result must
+be the same bytes on every run (the partial tiles are added in a fixed order whichever workgroup
+finishes last), the workspace's counters must be back at zero after every call so the workspace
+can be reused for the next shape, and shapes that are not split must run without a workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_act_amd import synth
+from oracle import mx_oracle as O
+
+from gpu_util import dev_bf16, dev_u8, host_bf16_bits, note, poison_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _workspace(mx, M, N, K):
+    n = mx.mx_gemm_splitk_workspace_size(M, N, K)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")     # torch allocations: 256-B aligned
+
+
+def _counters_zero(ws, M, N):
+    tiles = -(-M // 256) * -(-N // 256)
+    return int(ws[:tiles * 4].count_nonzero()) == 0
+
+
+def _operands(kind, M, N, K, seed, with_bias):
+    a_k, b_k = kind.split("_")
+    w = synth.gemm_inputs("acts" if a_k == "fp8" else "fp4", b_k, M, N, K, seed=seed,
+                          with_bias=with_bias, outlier_frac=0.01)
+    if w.a_kind == "acts":
+        a, a_s = O.act_quant(w.x)
+        A = O.decode_e4m3_rows(a, a_s)
+    else:
+        a, a_s = w.a, w.a_s
+        A = O.decode_fp4_rows(a, a_s)
+    B = O.decode_fp4_rows(w.b, w.b_s) if b_k == "fp4" else O.decode_fp8_block(w.b, w.b_s)
+    return w, a, a_s, A, B
+
+
+def _run(mx, kind, a, a_s, w, ws, M, N):
+    c = poison_bf16((M, N))
+    bias = None if w.bias is None else dev_bf16(w.bias)
+    getattr(mx, f"mx_gemm_{kind}_splitk")(dev_u8(a), dev_u8(a_s), dev_u8(w.b), dev_u8(w.b_s), c,
+                                          ws, bias=bias)
+    torch.cuda.synchronize()
+    return host_bf16_bits(c)
+
+
+def _check_full(out, A, B, w):
+    ref, S = O.gemm_ref(A, B, None if w.bias is None else O.bf16_to_f64(w.bias))
+    ok = O.within_tolerance(out, ref, S)
+    assert ok.all(), f"{np.count_nonzero(~ok)} of {ok.size} outside the bound"
+
+
+def _check_sampled(out, A, B, w, seed=7, n=6000):
+    """Random outputs plus every output of the first, last and tile-edge rows and columns."""
+    M, N = out.shape
+    rng = np.random.default_rng(seed)
+    edge_r = np.unique(np.clip([0, 255, 256, M - 1, M - 2], 0, M - 1))
+    edge_c = np.unique(np.clip([0, 255, 256, N - 1, N - 2], 0, N - 1))
+    rows = np.concatenate([rng.integers(0, M, n), np.repeat(edge_r, 64),
+                           rng.integers(0, M, 64 * len(edge_c))])
+    cols = np.concatenate([rng.integers(0, N, n), rng.integers(0, N, 64 * len(edge_r)),
+                           np.repeat(edge_c, 64)])
+    bias = None if w.bias is None else O.bf16_to_f64(w.bias)
+    ref, S = O.gemm_ref_at(A, B, rows, cols, bias)
+    ok = O.within_tolerance(out[rows, cols], ref, S)
+    assert ok.all(), f"{np.count_nonzero(~ok)} of {ok.size} sampled outputs outside the bound"
+    assert np.isfinite(O.bf16_to_f64(out)).all()
+
+
+# (M, N, K) that the plan splits (65..128 tiles of 256x256, >= 40 K steps per range): M and N
+# tails, a ragged last K step (5152 = 80.5 steps: ranges of 40 and 41), 88 and 65 tiles.
+SPLIT_SHAPES = [(2000, 4000, 5152), (1800, 2600, 6144), (1280, 3328, 5120)]
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_split_shapes_against_oracle(mx, kind, M, N, K, with_bias):
+    assert mx.mx_gemm_splitk_workspace_size(M, N, K) > 0            # these shapes are split
+    w, a, a_s, A, B = _operands(kind, M, N, K, seed=M + 3 * N + K + with_bias, with_bias=with_bias)
+    ws = _workspace(mx, M, N, K)
+    note(f"gemm splitk {kind} {M}x{N}x{K} bias={with_bias}")
+    out = _run(mx, kind, a, a_s, w, ws, M, N)
+    _check_sampled(out, A, B, w, seed=M + N)
+    assert _counters_zero(ws, M, N)
+
+
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8"])
+def test_repeatable_and_workspace_reused_across_shapes(mx, kind):
+    big = mx.mx_gemm_splitk_workspace_size(3072, 2048, 8192)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for (M, N, K) in [(3072, 2048, 8192), (1800, 2600, 6144), (3072, 2048, 8192),
+                      (1800, 2600, 6144), (3072, 2048, 8192)]:
+        assert 0 < mx.mx_gemm_splitk_workspace_size(M, N, K) <= big
+        w, a, a_s, A, B = _operands(kind, M, N, K, seed=5, with_bias=True)
+        note(f"gemm splitk repeat {kind} {M}x{N}x{K}")
+        out = _run(mx, kind, a, a_s, w, ws, M, N)
+        assert _counters_zero(ws, M, N)
+        if (M, N, K) in outs:
+            assert np.array_equal(out, outs[(M, N, K)])
+        else:
+            outs[(M, N, K)] = out
+            _check_sampled(out, A, B, w, n=2000)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("fp8_fp4", 4096, 2048, 7168), ("fp8_fp8", 3072, 2048, 8192),
+                                        ("fp4_fp4", 2048, 4096, 6144)])
+def test_down_projection_shapes_sampled(mx, kind, M, N, K):
+    w, a, a_s, A, B = _operands(kind, M, N, K, seed=11, with_bias=True)
+    ws = _workspace(mx, M, N, K)
+    assert ws is not None
+    note(f"gemm splitk {kind} {M}x{N}x{K}")
+    out = _run(mx, kind, a, a_s, w, ws, M, N)
+    assert _counters_zero(ws, M, N)
+    assert np.isfinite(O.bf16_to_f64(out)).all()
+    rng = np.random.default_rng(7)
+    rows, cols = rng.integers(0, M, 4000), rng.integers(0, N, 4000)
+    ref, S = O.gemm_ref_at(A, B, rows, cols, O.bf16_to_f64(w.bias))
+    assert O.within_tolerance(out[rows, cols], ref, S).all()
+    # the plain entry point on the same inputs: both within the bound (different sum orders)
+    c = poison_bf16((M, N))
+    getattr(mx, f"mx_gemm_{kind}")(dev_u8(a), dev_u8(a_s), dev_u8(w.b), dev_u8(w.b_s), c,
+                                   bias=dev_bf16(w.bias))
+    torch.cuda.synchronize()
+    plain = host_bf16_bits(c)
+    assert O.within_tolerance(plain[rows, cols], ref, S).all()
+
+
+def test_unsplit_shape_needs_no_workspace(mx):
+    M, N, K = 500, 3000, 512                           # 24 tiles, 8 K steps: not split
+    assert mx.mx_gemm_splitk_workspace_size(M, N, K) == 0
+    w, a, a_s, A, B = _operands("fp8_fp4", M, N, K, seed=2, with_bias=True)
+    note("gemm splitk unsplit shape")
+    out = _run(mx, "fp8_fp4", a, a_s, w, None, M, N)
+    _check_full(out, A, B, w)
+
+
+def test_split_shape_without_workspace_is_refused(mx):
+    w, a, a_s, A, B = _operands("fp8_fp4", 1280, 3328, 5120, seed=3, with_bias=False)
+    with pytest.raises(mx.MxError) as e:
+        _run(mx, "fp8_fp4", a, a_s, w, None, 1280, 3328)
+    assert e.value.status == mx.MX_ERR_WORKSPACE
