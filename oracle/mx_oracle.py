@@ -514,3 +514,191 @@ def gelu_within(out_bits, pre, S) -> np.ndarray:
     S = np.asarray(S, dtype=np.float64)
     ok = np.abs(out - g) <= np.ldexp(np.abs(g), -7) + np.ldexp(S, -19) + np.ldexp(1.0, -126)
     return ok & np.isfinite(out)
+
+
+# ----------------------------------------------------------------------------------------------
+# O7: backward-pass operands: E5M2 gradients (round-to-nearest-even or stochastic) and
+#     quantize-transpose
+# ----------------------------------------------------------------------------------------------
+# The hip_quant page's "FP8 Formats" table gives E5M2 as 1 sign, 5 exponent, 2 mantissa bits,
+# bias 15, max 57344, with Inf and NaN; its default rounding is round-to-nearest-even, and its
+# opt-in stochastic rounding for backward gradients rounds between the two neighbouring E5M2
+# values with probability proportional to the distance, using a stateless per-element hash of
+# (seed, element index).  It also offers quantize-plus-transpose for rank-2 tensors, and block-
+# wise E5M2 with one scale per 32 values along the last dimension; the AstrAI page routes the
+# weight and input gradients through the forward GEMM via contiguous transposes.  Readings (each
+# is listed with the others):
+#   scale: act_quant's rule with E5M2's largest magnitude 57344: E = ceil(log2(amax / 57344))
+#       exactly, amax floored at the smallest normal float32 (a gradient block may be far
+#       below act_quant's 1e-4 floor), E clamped to E8M0's least exponent -127;
+#   stochastic rounding: with lo <= |y| < hi the neighbouring E5M2 magnitudes, the result is hi
+#       when u < 2^32 (|y| - lo) / (hi - lo), else lo, for a 32-bit uniform u;
+#   the hash: Philox4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
+#       SC 2011) with key (seed, 0) and counter (i >> 3, 0, 0, 0); the element with index i takes
+#       32-bit word i & 7 of the block (64-bit output word (i & 7) >> 1, low half first);
+#   the element index is the position of the code in the quantized output (row-major), so a
+#       transposed output draws by its own layout.
+
+E5M2_MAX = 57344.0
+E5M2_SPECIAL = tuple(range(0x7C, 0x80)) + tuple(range(0xFC, 0x100))    # Inf and NaN codes
+
+
+def e5m2_to_f64(codes) -> np.ndarray:
+    """E5M2 code -> value from its bit fields (hip_quant page, FP8 Formats table): sign bit 7,
+    exponent bits 6..2 with bias 15, 2 mantissa bits; exponent 0 is subnormal, m * 2^-16.
+    Inf and NaN codes (exponent 31) are refused."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if np.any(np.isin(c, E5M2_SPECIAL)):
+        raise OracleRefusal("E5M2 Inf/NaN code")
+    s = (c >> 7).astype(np.int64)
+    e = ((c >> 2) & 0x1F).astype(np.int64)
+    m = (c & 3).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -16, np.ldexp(1.0 + m / 4.0, e - 15))
+    return np.where(s == 1, -mag, mag)
+
+
+def _e5m2_grid() -> np.ndarray:
+    """The 124 non-negative finite E5M2 magnitudes in increasing order (codes 0x00..0x7B)."""
+    return e5m2_to_f64(np.arange(0x7C, dtype=np.uint8))
+
+
+def e5m2_encode_rne(y) -> np.ndarray:
+    """Nearest E5M2 code to each float64 y with |y| <= 57344, ties to the even code, sign kept."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(~np.isfinite(y)) or np.any(np.abs(y) > E5M2_MAX):
+        raise OracleRefusal("e5m2_encode_rne expects finite |y| <= 57344")
+    grid = _e5m2_grid()
+    a = np.abs(y)
+    hi = np.minimum(np.searchsorted(grid, a, side="left"), len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == grid[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return code | np.where(np.signbit(y), 0x80, 0).astype(np.uint8)
+
+
+def grad_scale_bytes(x_bits) -> np.ndarray:
+    """Per-32 E8M0 bytes of the gradient quantizer: E + 127, E = ceil(log2(amax / 57344)) exactly,
+    amax (float32, from bf16) floored at 2^-126, E clamped to >= -127.  E starts from
+    floor(log2 amax) - 15 (frexp, exact) and is raised while amax > 57344 * 2^E."""
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    K = x.shape[-1]
+    if K % BLOCK:
+        raise OracleRefusal(f"gradient quantizer: last dim {K} not a multiple of {BLOCK}")
+    if not np.all(np.isfinite(x)):
+        raise OracleRefusal("gradient quantizer: non-finite value")
+    xb = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK))
+    amax = np.maximum(np.abs(xb).max(axis=-1), np.float32(2.0 ** -126)).astype(np.float64)
+    _, ex = np.frexp(amax)
+    E = (ex - 1 - 15).astype(np.int64)
+    for _ in range(2):
+        E = E + (amax > E5M2_MAX * np.ldexp(1.0, E))
+    return (np.maximum(E, -127) + 127).astype(np.uint8)
+
+
+_M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
+_LO32 = np.uint64(0xFFFFFFFF)
+PHILOX_M0, PHILOX_M1 = 0xD2E7470EE14C6C93, 0xCA5A826395121157    # round multipliers
+PHILOX_W0, PHILOX_W1 = 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B    # key increments (Weyl)
+
+
+def _mulhilo64(a: np.ndarray, m: int):
+    """(high, low) 64-bit halves of the 128-bit product a * m, from 32-bit pieces."""
+    a = a.astype(np.uint64)
+    a0, a1 = a & _LO32, a >> np.uint64(32)
+    m0, m1 = np.uint64(m & 0xFFFFFFFF), np.uint64(m >> 32)
+    p00, p01, p10, p11 = a0 * m0, a0 * m1, a1 * m0, a1 * m1
+    mid = (p00 >> np.uint64(32)) + (p01 & _LO32) + (p10 & _LO32)
+    lo = (mid << np.uint64(32)) | (p00 & _LO32)
+    hi = p11 + (p01 >> np.uint64(32)) + (p10 >> np.uint64(32)) + (mid >> np.uint64(32))
+    return hi, lo
+
+
+def philox4x64_10(ctr, key):
+    """Philox4x64 with 10 rounds (Salmon et al., SC 2011): ctr a tuple of 4 uint64 arrays, key a
+    tuple of 2 uint64 values; returns the 4 output words.  A round maps (x0, x1, x2, x3) with
+    (h0, l0) = M0 * x0 and (h1, l1) = M1 * x2 to (h1 ^ x1 ^ k0, l1, h0 ^ x3 ^ k1, l0); the key
+    advances by (W0, W1) between rounds."""
+    with np.errstate(over="ignore"):
+        x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) for c in ctr)
+        k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+        for r in range(10):
+            if r:
+                k0 = np.uint64((int(k0) + PHILOX_W0) & 0xFFFFFFFFFFFFFFFF)
+                k1 = np.uint64((int(k1) + PHILOX_W1) & 0xFFFFFFFFFFFFFFFF)
+            h0, l0 = _mulhilo64(x0, PHILOX_M0)
+            h1, l1 = _mulhilo64(x2, PHILOX_M1)
+            x0, x1, x2, x3 = h1 ^ x1 ^ k0, l1, h0 ^ x3 ^ k1, l0
+    return x0, x1, x2, x3
+
+
+def uniform_u32(seed: int, idx) -> np.ndarray:
+    """The 32-bit uniform of element index idx: word idx & 7 of Philox4x64-10 block idx >> 3
+    under key (seed, 0) (64-bit output word (idx & 7) >> 1, low half first)."""
+    idx = np.asarray(idx, dtype=np.uint64)
+    z = np.zeros_like(idx)
+    w = philox4x64_10((idx >> np.uint64(3), z, z, z), (np.uint64(seed), np.uint64(0)))
+    k = (idx & np.uint64(7)).astype(np.int64)
+    word = np.choose(k >> 1, w)
+    return ((word >> (np.uint64(32) * (k & 1).astype(np.uint64))) & _LO32).astype(np.uint64)
+
+
+def e5m2_encode_stochastic(y, u) -> np.ndarray:
+    """Stochastic E5M2 code of each float64 y (|y| <= 57344) under 32-bit uniforms u: with
+    lo <= |y| < hi the neighbouring E5M2 magnitudes, hi when u < 2^32 (|y| - lo) / (hi - lo),
+    else lo (|y| on the grid is kept); the sign of y is kept.  All quantities are dyadic, so the
+    comparison is exact in float64."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(~np.isfinite(y)) or np.any(np.abs(y) > E5M2_MAX):
+        raise OracleRefusal("e5m2_encode_stochastic expects finite |y| <= 57344")
+    u = np.asarray(u, dtype=np.uint64).astype(np.float64)           # exact: < 2^53
+    grid = _e5m2_grid()
+    a = np.abs(y)
+    lo = np.searchsorted(grid, a, side="right") - 1                  # grid[lo] <= a
+    on = grid[lo] == a
+    hi = np.minimum(lo + 1, len(grid) - 1)
+    width = np.where(on, 1.0, grid[hi] - grid[lo])
+    up = ~on & (u < np.ldexp((a - grid[lo]) / width, 32))
+    code = np.where(up, hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(y), 0x80, 0).astype(np.uint8)
+
+
+def grad_quant_e5m2(x_bits, seed=None) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 gradients [..., K] -> (E5M2 codes [..., K], E8M0 bytes [..., K/32]) per 32 along the
+    last dimension: y = x / 2^E (exact), then round-to-nearest-even (seed None) or stochastic
+    rounding with u = uniform_u32(seed, i), i the element's row-major index in the output."""
+    x = bf16_to_f64(x_bits)
+    sb = grad_scale_bytes(x_bits)
+    K = x.shape[-1]
+    y = (x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK)) / e8m0_to_f64(sb)[..., None]).reshape(x.shape)
+    if seed is None:
+        codes = e5m2_encode_rne(y)
+    else:
+        u = uniform_u32(seed, np.arange(y.size, dtype=np.uint64)).reshape(y.shape)
+        codes = e5m2_encode_stochastic(y, u)
+    return codes, sb
+
+
+def quant_transpose_e4m3(x_bits) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 [R, C] -> act_quant of its transpose: E4M3 codes [C, R] and E8M0 bytes [C, R/32], the
+    32-blocks running along R (the contraction dimension of a GEMM that reads the transpose)."""
+    x = np.asarray(x_bits)
+    if x.ndim != 2:
+        raise OracleRefusal("quant_transpose expects a rank-2 tensor")
+    return act_quant(np.ascontiguousarray(x.T))
+
+
+def quant_transpose_e5m2(x_bits, seed=None) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 [R, C] -> grad_quant_e5m2 of its transpose (codes [C, R], bytes [C, R/32]); the
+    stochastic draw uses each code's index in that [C, R] output."""
+    x = np.asarray(x_bits)
+    if x.ndim != 2:
+        raise OracleRefusal("quant_transpose expects a rank-2 tensor")
+    return grad_quant_e5m2(np.ascontiguousarray(x.T), seed)
+
+
+def decode_e5m2_rows(codes, scale_bytes) -> np.ndarray:
+    """E5M2 codes [..., K] with per-row-32 scales [..., K/32] -> float64 values."""
+    v = e5m2_to_f64(codes)
+    s = np.repeat(e8m0_to_f64(scale_bytes), BLOCK, axis=-1)
+    return v * s
