@@ -39,6 +39,7 @@ ACT_QUANT_FP4_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, half a byte of E2M1
 
 
 GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip",
+                "block_scaled_precision_act_amd/csrc/mx_internal.h",
                 "block_scaled_precision_act_amd/csrc/mx_epilogue.h",
                 "block_scaled_precision_act_amd/csrc/mx_quant.h"]
 ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip",
@@ -264,6 +265,11 @@ def main():
               "speedup": round(plain_ms / split_ms, 3), "workspace_bytes": int(wsd.numel())}
     del ad, asd, bd, bsd, biasd, cd, wsd
 
+    # ---- the backward of the same linear layer y = x W^T (x [4096, 2048], W [7168, 2048],
+    # dY [4096, 7168]): dX = dY W and dW = dY^T x from stochastically rounded E5M2 gradients and
+    # transposed E4M3 operands, six kernels on one stream
+    backward = bench_backward(mx, synth, torch, dev_bf16, w.x, stream)
+
     # ---- standalone act_quant on [16384, 7168], sustained: back-to-back launches rotating over
     # three input/output sets (1.07 GB, far beyond the 256 MB last-level cache), so each launch
     # reads its input from HBM and pays for the previous launch's write-back.
@@ -343,11 +349,67 @@ def main():
     out["next_layer_quant"] = next_layer
     out["epilogues"] = epilogues
     out["splitk"] = splitk
+    out["backward"] = backward
     if others is not None:
         out["other_configs"] = others
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+def bench_backward(mx, synth, torch, dev_bf16, x_bits, stream):
+    """dX and dW of the 4096x7168x2048 linear layer: each kernel over 50 back-to-back launches,
+    then the whole six-kernel backward step."""
+    M, K = x_bits.shape
+    N = 7168
+    rng = synth.rng_for(1007)
+    W = dev_bf16(synth.bf16_normal(rng, (N, K), std=0.05))
+    dY = dev_bf16(synth.bf16_normal(rng, (M, N), std=1e-3))
+    x = dev_bf16(x_bits)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    gq, gs = torch.empty((M, N), **u8), torch.empty((M, N // 32), **u8)
+    wq, wsc = torch.empty((K, N), **u8), torch.empty((K, N // 32), **u8)
+    gtq, gts = torch.empty((N, M), **u8), torch.empty((N, M // 32), **u8)
+    xq, xs = torch.empty((K, M), **u8), torch.empty((K, M // 32), **u8)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(max(mx.mx_gemm_splitk_workspace_size(M, K, N), 256), **u8)
+    steps = {
+        "quant_e5m2_dY": lambda: mx.mx_quant_e5m2(dY, gq, gs, seed=1234, stream=stream),
+        "quant_transpose_e4m3_W": lambda: mx.mx_quant_transpose_e4m3(W, wq, wsc, stream=stream),
+        "gemm_dX_splitk": lambda: mx.mx_gemm_e5m2_e4m3_splitk(gq, gs, wq, wsc, dX, ws, stream=stream),
+        "quant_transpose_e5m2_dY": lambda: mx.mx_quant_transpose_e5m2(dY, gtq, gts, seed=4321,
+                                                                      stream=stream),
+        "quant_transpose_e4m3_x": lambda: mx.mx_quant_transpose_e4m3(x, xq, xs, stream=stream),
+        "gemm_dW": lambda: mx.mx_gemm_e5m2_e4m3(gtq, gts, xq, xs, dW, stream=stream),
+    }
+
+    def step():
+        for f in steps.values():
+            f()
+
+    for _ in range(100):
+        step()
+    res = {"workload": "backward of y = x W^T, x [4096, 2048], W [7168, 2048], dY [4096, 7168]: "
+                       "dX = dY W (K split), dW = dY^T x; stochastic E5M2 gradients"}
+    qbytes = {"quant_e5m2_dY": M * N, "quant_transpose_e4m3_W": N * K,
+              "quant_transpose_e5m2_dY": M * N, "quant_transpose_e4m3_x": M * K}
+    flops = 2.0 * M * N * K
+    for name, f in steps.items():
+        ms = time_events(f, 50, torch)
+        entry = {"ms": round(ms, 5)}
+        if name in qbytes:
+            entry["gbs"] = round(ACT_QUANT_BYTES_PER_ELEM * qbytes[name] / (ms * 1e-3) / 1e9, 1)
+        else:
+            entry["tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+        res[name] = entry
+    rne_ms = time_events(lambda: mx.mx_quant_e5m2(dY, gq, gs, stream=stream), 50, torch)
+    res["quant_e5m2_dY_round_to_nearest"] = {
+        "ms": round(rne_ms, 5), "gbs": round(ACT_QUANT_BYTES_PER_ELEM * M * N / (rne_ms * 1e-3) / 1e9, 1)}
+    step_ms = time_events(step, 20, torch)
+    res["step_ms"] = round(step_ms, 5)
+    res["step_tflops"] = round(2 * flops / (step_ms * 1e-3) / 1e12, 2)
+    return res
 
 
 def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):

@@ -57,6 +57,15 @@ for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
                                                         _I, _I, _I, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_splitk"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]
 _SIGS["mx_gemm_splitk_workspace_size"] = [_I, _I, _I]
+_U64, _C = ctypes.c_uint64, ctypes.c_int
+_SIGS["mx_quant_e5m2"] = [_P, _P, _P, _I, _I, _C, _U64, _P]
+_SIGS["mx_quant_e5m2_strided_batched"] = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _C, _U64, _P]
+_SIGS["mx_quant_transpose_e4m3"] = [_P, _P, _P, _I, _I, _P]
+_SIGS["mx_quant_transpose_e5m2"] = [_P, _P, _P, _I, _I, _C, _U64, _P]
+_SIGS["mx_gemm_e5m2_e4m3"] = [_P, _P, _P, _P, _P, _I, _I, _I, _P]
+_SIGS["mx_gemm_e5m2_e4m3_splitk"] = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]
+_SIGS["mx_gemm_e5m2_e4m3_strided_batched"] = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                              _I, _P]
 for _n in ("fp8_fp4", "fp8_fp8"):
     _SIGS[f"mx_gemm_{_n}_quant"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_quant_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -305,3 +314,60 @@ def mx_gemm_fp8_fp8_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None)
 def mx_gemm_fp4_fp4_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None):
     """As mx_gemm_fp8_fp4_splitk for MXFP4 activations."""
     _gemm_splitk("fp4_fp4", a, a_s, b, b_s, c, workspace, bias, stream)
+
+
+def mx_quant_e5m2(x, q, s, seed=None, stream=None):
+    """Gradients x: bf16 [(B,) M, K] -> q: E5M2 [(B,) M, K], s: E8M0 [(B,) M, K/32]; round to
+    nearest even (seed None) or stochastically from Philox4x64-10 under `seed`."""
+    st, sd = (0, 0) if seed is None else (1, int(seed))
+    M, K = x.shape[-2], x.shape[-1]
+    if x.dim() == 2:
+        _check("mx_quant_e5m2", load().mx_quant_e5m2(_ptr(x), _ptr(q), _ptr(s), M, K, st, sd,
+                                                     _stream(stream)))
+    else:
+        _check("mx_quant_e5m2_strided_batched",
+               load().mx_quant_e5m2_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, x.shape[0],
+                                                    x.stride(0), q.stride(0), s.stride(0), st, sd,
+                                                    _stream(stream)))
+
+
+def mx_quant_transpose_e4m3(x, q, s, stream=None):
+    """x: bf16 [R, C] -> q: E4M3 [C, R], s: E8M0 [C, R/32] (act_quant of x^T)."""
+    R, C = x.shape
+    _check("mx_quant_transpose_e4m3",
+           load().mx_quant_transpose_e4m3(_ptr(x), _ptr(q), _ptr(s), R, C, _stream(stream)))
+
+
+def mx_quant_transpose_e5m2(x, q, s, seed=None, stream=None):
+    """x: bf16 [R, C] -> q: E5M2 [C, R], s: E8M0 [C, R/32] (mx_quant_e5m2 of x^T)."""
+    R, C = x.shape
+    st, sd = (0, 0) if seed is None else (1, int(seed))
+    _check("mx_quant_transpose_e5m2",
+           load().mx_quant_transpose_e5m2(_ptr(x), _ptr(q), _ptr(s), R, C, st, sd,
+                                          _stream(stream)))
+
+
+def mx_gemm_e5m2_e4m3(a, a_s, b, b_s, c, stream=None):
+    """a: E5M2 [(B,) M, K] + a_s [(B,) M, K/32]; b: E4M3 [(B,) N, K] + b_s [(B,) N, K/32] (per-row
+    scales); c: bf16 [(B,) M, N] = a b^T."""
+    M, N, K = c.shape[-2], c.shape[-1], a.shape[-1]
+    lib = load()
+    if c.dim() == 2:
+        _check("mx_gemm_e5m2_e4m3", lib.mx_gemm_e5m2_e4m3(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
+                                                          _ptr(c), M, N, K, _stream(stream)))
+    else:
+        strides = [t.stride(0) if t.dim() == 3 else 0 for t in (a, a_s, b, b_s)]
+        _check("mx_gemm_e5m2_e4m3_strided_batched",
+               lib.mx_gemm_e5m2_e4m3_strided_batched(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
+                                                     _ptr(c), M, N, K, c.shape[0], *strides,
+                                                     c.stride(0), _stream(stream)))
+
+
+def mx_gemm_e5m2_e4m3_splitk(a, a_s, b, b_s, c, workspace, stream=None):
+    """As mx_gemm_e5m2_e4m3 (single problem) with K split across workgroups for shapes with few
+    output tiles; workspace as for mx_gemm_fp8_fp4_splitk (None where the shape is not split)."""
+    M, N, K = c.shape[0], c.shape[1], a.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mx_gemm_e5m2_e4m3_splitk",
+           load().mx_gemm_e5m2_e4m3_splitk(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c), M, N,
+                                           K, _ptr(workspace), ws_bytes, _stream(stream)))

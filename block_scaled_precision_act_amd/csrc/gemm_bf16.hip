@@ -115,6 +115,16 @@ __device__ __forceinline__ uint4 decode_fp8_pair(uint32_t lo, uint32_t hi, float
   return o;
 }
 
+// 8 E5M2 codes (two dwords) times s -> 8 bf16.
+__device__ __forceinline__ uint4 decode_bf8_pair(uint32_t lo, uint32_t hi, float s) {
+  uint4 o;
+  o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, s, false));
+  o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, s, true));
+  o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, s, false));
+  o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, s, true));
+  return o;
+}
+
 // Decoded rows are 128 B (64 bf16 = 8 chunks of 16 B).  Chunk c of row r is stored at chunk
 // c ^ swz(r), swz(r) = (r & 7) ^ parity(bits 1..3 of r), period 16 in r.  It keeps every LDS pass
 // free of bank conflicts, whether a pass serves 8 lanes (128 B of banks) or 16 lanes (256 B), for
@@ -135,7 +145,7 @@ __device__ __forceinline__ uint32_t lds_offset(int row, int chunk) {
 // 16 distinct 16-byte bank groups.  Period 16 in r.
 template <int FMT>
 __device__ __forceinline__ int graw(int row) {
-  return FMT == kFp8 ? (row >> 2) & 3 : (row >> 3) & 1;
+  return byte_codes(FMT) ? (row >> 2) & 3 : (row >> 3) & 1;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -155,13 +165,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // the step after next, so every piece has a whole K step to arrive with a single register set.
 template <int FMT, int ROWS, int NT, bool DECODE, int PART0, int NPART>
 struct Stager {
-  static constexpr int kPieces = FMT == kFp8 ? 4 : 2;
-  static constexpr int kStepBytes = FMT == kFp8 ? 64 : 32;       // bytes of a row per K step
+  static constexpr int kPieces = byte_codes(FMT) ? 4 : 2;
+  static constexpr int kStepBytes = byte_codes(FMT) ? 64 : 32;   // bytes of a row per K step
   static constexpr int kTotal = ROWS * kPieces;
   static constexpr int kPer = (kTotal + NT - 1) / NT;
   static constexpr bool kAll = kTotal % NT == 0;
   static constexpr int kRowStride = NT / kPieces;                // rows between pieces i, i+1
-  static constexpr int kChunksPerPiece = DECODE ? (FMT == kFp8 ? 2 : 4) : 1;
+  static constexpr int kChunksPerPiece = DECODE ? (byte_codes(FMT) ? 2 : 4) : 1;
   static constexpr int kChunks = kPer * kChunksPerPiece;
   static constexpr uint32_t kOob = 0x80000000u;                  // past any buffer bound
   static_assert(NT % kPieces == 0 && kRowStride % 16 == 0, "swizzle period");
@@ -177,11 +187,11 @@ struct Stager {
 
   __device__ __forceinline__ void init(const uint8_t* base, const uint8_t* sbase, int row0,
                                        int rows_valid, int K, bool block_scales, uint32_t region) {
-    const int pitch = FMT == kFp8 ? K : K / 2;
+    const int pitch = byte_codes(FMT) ? K : K / 2;
     const int kb_total = K / 32;
     const int t = threadIdx.x;
     const int p = t % kPieces;
-    const int koff = (FMT == kFp8 ? 16 : 32) * p;
+    const int koff = (byte_codes(FMT) ? 16 : 32) * p;
     upper = koff >= 32;
     const int srows = block_scales ? (rows_valid + 31) / 32 : rows_valid;
     codes = make_rsrc(base, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(pitch));
@@ -235,7 +245,9 @@ struct Stager {
       const uint32_t c0 = (lds0 >> 4) & 7;
       uint8_t* dst = stage + (lds0 - (c0 << 4)) + i * kRowStride * kRowBytes + ((c0 ^ j) << 4);
       uint4 o;
-      if constexpr (FMT == kFp8) {
+      if constexpr (FMT == kBf8) {
+        o = j == 0 ? decode_bf8_pair(raw[i].x, raw[i].y, s) : decode_bf8_pair(raw[i].z, raw[i].w, s);
+      } else if constexpr (byte_codes(FMT)) {
         o = j == 0 ? decode_fp8_pair(raw[i].x, raw[i].y, s) : decode_fp8_pair(raw[i].z, raw[i].w, s);
       } else {
         const uint32_t d = j == 0 ? raw[i].x : j == 1 ? raw[i].y : j == 2 ? raw[i].z : raw[i].w;
@@ -287,8 +299,8 @@ struct Stager {
 // each sub-step into the MFMA's bf16 operand just before they are needed.
 template <int BF, int TN>
 struct BRegs {
-  static constexpr int kQ = BF == kFp8 ? 2 : 1;        // 16-byte units per row per lane
-  static constexpr int kPitch = BF == kFp8 ? 64 : 32;  // raw row bytes per step
+  static constexpr int kQ = byte_codes(BF) ? 2 : 1;        // 16-byte units per row per lane
+  static constexpr int kPitch = byte_codes(BF) ? 64 : 32;  // raw row bytes per step
   uint4 raw[TN][kQ];
   float scale[TN];
   uint32_t sbyte[TN];           // scale bytes of the step loaded next
@@ -300,7 +312,7 @@ struct BRegs {
                                        uint32_t region, int row_local) {
     const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
     const int kb_total = K / 32;
-    const int srows = BF == kFp8 ? (N + 31) / 32 : N;
+    const int srows = BF == kFp8 ? (N + 31) / 32 : N;    // 32x32 blocks, or per row
     srsrc = make_rsrc(sbase, static_cast<uint32_t>(srows) * static_cast<uint32_t>(kb_total));
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -311,7 +323,7 @@ struct BRegs {
     const int r = row_local + l32;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const int u = BF == kFp8 ? 2 * h + q : h;
+      const int u = byte_codes(BF) ? 2 * h + q : h;
       lds_off[q] = region + static_cast<uint32_t>(r * kPitch + ((u ^ graw<BF>(r)) << 4));
     }
   }
@@ -342,7 +354,7 @@ struct BRegs {
   template <int S, int J>
   __device__ __forceinline__ void decode(bf16x8& out) const {
     uint4 o;
-    if constexpr (BF == kFp8) {
+    if constexpr (byte_codes(BF)) {
       const uint4 q = raw[J][S >> 1];
       o = (S & 1) ? decode_fp8_pair(q.z, q.w, scale[J]) : decode_fp8_pair(q.x, q.y, scale[J]);
     } else {
@@ -455,7 +467,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   constexpr int WTM = BM / WM, WTN = BN / WN;     // WM x WN wavefronts
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  constexpr int kBPitch = BF == kFp8 ? 64 : 32;
+  constexpr int kBPitch = byte_codes(BF) ? 64 : 32;
   constexpr int kBRegion = BM * kRowBytes;
   constexpr int kStageBytes = kBRegion + BN * kBPitch;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -716,7 +728,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
 
 template <int AF, int BF, int BM, int BN>
 constexpr int lds_bytes() {
-  constexpr int stages = 2 * (BM * kRowBytes + BN * (BF == kFp8 ? 64 : 32));
+  constexpr int stages = 2 * (BM * kRowBytes + BN * (byte_codes(BF) ? 64 : 32));
   constexpr int tile = BM * BN * 2;
   return stages > tile ? stages : tile;
 }
@@ -803,6 +815,7 @@ hipError_t launch_gemm_bf16(int a_fmt, int b_fmt, const GemmProblem& p, const De
   if (a_fmt == kFp8 && b_fmt == kFp4) return launch_formats<kFp8, kFp4>(p, dev, stream);
   if (a_fmt == kFp8 && b_fmt == kFp8) return launch_formats<kFp8, kFp8>(p, dev, stream);
   if (a_fmt == kFp4 && b_fmt == kFp4) return launch_formats<kFp4, kFp4>(p, dev, stream);
+  if (a_fmt == kBf8 && b_fmt == kFp8Rows) return launch_formats<kBf8, kFp8Rows>(p, dev, stream);
   return hipErrorInvalidValue;
 }
 

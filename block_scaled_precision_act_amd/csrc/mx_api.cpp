@@ -90,14 +90,32 @@ int validate_act_quant(const void* x, void* q, void* s, int64_t M, int64_t K, in
 }
 
 int act_quant_impl(const void* x, void* q, void* s, int64_t M, int64_t K, int64_t batch,
-                   int64_t sx, int64_t sq, int64_t ss, void* stream, int fmt = mx::kFp8) {
+                   int64_t sx, int64_t sq, int64_t ss, void* stream, int fmt = mx::kFp8,
+                   bool stochastic = false, uint64_t seed = 0) {
   int st = validate_act_quant(x, q, s, M, K, batch, sx, sq, ss);
   if (st != MX_OK || M == 0 || batch == 0) return st;
   DeviceInfo dev;
   if ((st = device_status(&dev)) != MX_OK) return st;
   hipError_t e = mx::launch_act_quant(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q),
                                       static_cast<uint8_t*>(s), M, K, batch, sx, sq, ss,
-                                      static_cast<hipStream_t>(stream), fmt);
+                                      static_cast<hipStream_t>(stream), fmt, stochastic, seed);
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int quant_transpose_impl(const void* x, void* q, void* s, int64_t R, int64_t C, void* stream,
+                         int fmt, bool stochastic, uint64_t seed) {
+  if (R < 0 || C < 0 || R % 32 != 0 || C % 8 != 0) return MX_ERR_SHAPE;
+  if (R > 0 && C > mx::kMaxMatrixElems / R) return MX_ERR_SHAPE;
+  if (R == 0 || C == 0) return MX_OK;
+  if (!x || !q || !s) return MX_ERR_NULL;
+  if (!mx::aligned16(x) || !mx::aligned16(q)) return MX_ERR_ALIGN;
+  int st;
+  DeviceInfo dev;
+  if ((st = device_status(&dev)) != MX_OK) return st;
+  hipError_t e = mx::launch_quant_transpose(static_cast<const uint16_t*>(x),
+                                            static_cast<uint8_t*>(q), static_cast<uint8_t*>(s),
+                                            R, C, static_cast<hipStream_t>(stream), fmt,
+                                            stochastic, seed);
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
@@ -293,6 +311,51 @@ int mx_act_quant_fp4_strided_batched(const void* x, void* q, void* s, int64_t M,
                                      int64_t batch, int64_t stride_x, int64_t stride_q,
                                      int64_t stride_s, void* stream) {
   return act_quant_impl(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream, mx::kFp4);
+}
+
+int mx_quant_e5m2(const void* x, void* q, void* s, int64_t M, int64_t K, int stochastic,
+                  uint64_t seed, void* stream) {
+  return act_quant_impl(x, q, s, M, K, 1, 0, 0, 0, stream, mx::kBf8, stochastic != 0, seed);
+}
+
+int mx_quant_e5m2_strided_batched(const void* x, void* q, void* s, int64_t M, int64_t K,
+                                  int64_t batch, int64_t stride_x, int64_t stride_q,
+                                  int64_t stride_s, int stochastic, uint64_t seed, void* stream) {
+  return act_quant_impl(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream, mx::kBf8,
+                        stochastic != 0, seed);
+}
+
+int mx_quant_transpose_e4m3(const void* x, void* q, void* s, int64_t R, int64_t C, void* stream) {
+  return quant_transpose_impl(x, q, s, R, C, stream, mx::kFp8, false, 0);
+}
+
+int mx_quant_transpose_e5m2(const void* x, void* q, void* s, int64_t R, int64_t C, int stochastic,
+                            uint64_t seed, void* stream) {
+  return quant_transpose_impl(x, q, s, R, C, stream, mx::kBf8, stochastic != 0, seed);
+}
+
+int mx_gemm_e5m2_e4m3(const void* a, const void* a_s, const void* b, const void* b_s, void* c,
+                      int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_impl(single(mx::kBf8, mx::kFp8Rows, a, a_s, b, b_s, nullptr, c, M, N, K, false),
+                   stream);
+}
+
+int mx_gemm_e5m2_e4m3_splitk(const void* a, const void* a_s, const void* b, const void* b_s,
+                             void* c, int64_t M, int64_t N, int64_t K, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  return gemm_impl(with_workspace(single(mx::kBf8, mx::kFp8Rows, a, a_s, b, b_s, nullptr, c, M, N,
+                                         K, false),
+                                  workspace, workspace_bytes),
+                   stream);
+}
+
+int mx_gemm_e5m2_e4m3_strided_batched(const void* a, const void* a_s, const void* b,
+                                      const void* b_s, void* c, int64_t M, int64_t N, int64_t K,
+                                      int64_t batch, int64_t sa, int64_t sas, int64_t sb,
+                                      int64_t sbs, int64_t sc, void* stream) {
+  return gemm_impl(batched(mx::kBf8, mx::kFp8Rows, a, a_s, b, b_s, nullptr, c, M, N, K, batch, sa,
+                           sas, sb, sbs, 0, sc, false),
+                   stream);
 }
 
 #define MX_GEMM_ENTRY_POINTS(NAME, AF, BF)                                                    \

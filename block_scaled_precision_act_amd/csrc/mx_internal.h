@@ -8,7 +8,13 @@
 namespace mx {
 
 // Operand encodings, numbered as the scaled f8f6f4 MFMA's format fields number them.
-enum OperandFmt : int { kFp8 = 0, kFp4 = 4 };
+// kBf8 is E5M2 (backward gradients).  kFp8Rows is not an MFMA format: E4M3 codes whose E8M0
+// scales run per row and 32 K (as activations'), where a kFp8 weight has 32x32 block scales; the
+// backward GEMMs read transposed operands in that layout.
+enum OperandFmt : int { kFp8 = 0, kBf8 = 1, kFp4 = 4, kFp8Rows = 8 };
+
+// One code byte per value (E4M3 or E5M2), against packed E2M1.
+constexpr bool byte_codes(int fmt) { return fmt != kFp4; }
 
 // What the epilogue does to (sum + bias) before the single bf16 rounding.
 enum Epilogue : int {
@@ -78,10 +84,18 @@ struct DeviceInfo {
 // Cached per-device properties of the calling thread's current device (false: no device).
 bool current_device(DeviceInfo* info);
 
-// fmt: kFp8 (E4M3 codes [M, K]) or kFp4 (packed E2M1 [M, K/2]); scales E8M0 [M, K/32].
+// fmt: kFp8 (E4M3 codes [M, K]), kFp4 (packed E2M1 [M, K/2]) or kBf8 (E5M2 codes [M, K], rounded
+// to nearest even, or stochastically with `seed` when `stochastic`); scales E8M0 [M, K/32].
 hipError_t launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
                             int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
-                            hipStream_t stream, int fmt = kFp8);
+                            hipStream_t stream, int fmt = kFp8, bool stochastic = false,
+                            uint64_t seed = 0);
+
+// Quantize-transpose: bf16 x [R, C] -> codes [C, R] + E8M0 [C, R/32] (blocks along R), E4M3 with
+// act_quant's rule (fmt kFp8) or E5M2 with the gradient rule (fmt kBf8, RNE or stochastic).
+// R % 32 == 0, C % 8 == 0, x and q 16-byte aligned.
+hipError_t launch_quant_transpose(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t R, int64_t C,
+                                  hipStream_t stream, int fmt, bool stochastic, uint64_t seed);
 
 // FP8-operand kinds: exact bf16 decode + bf16 MFMA (gemm_bf16.hip).
 hipError_t launch_gemm_bf16(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,

@@ -340,6 +340,58 @@ int mx_gemm_fp4_fp4_splitk(const void* a, const void* a_scale, const void* b, co
                            const void* bias, void* c, int64_t M, int64_t N, int64_t K,
                            void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Backward-pass operands and GEMM (E5M2 gradients).
+ *
+ * The hip_quant page uses E4M3 for forward activations and weights and E5M2 (1 sign, 5 exponent
+ * bits with bias 15, 2 mantissa bits, largest magnitude 57344; FP8 Formats table) for backward
+ * gradients, rounded to nearest even or, opt-in, stochastically: between the two neighbouring
+ * E5M2 values with chances that follow the distances, from a hash of the seed and the element's
+ * index (section "Stochastic E5M2 Backward Gradients"); it also quantizes with a
+ * fused transpose for rank-2 tensors.  The AstrAI page routes a linear layer's input and weight
+ * gradients through the forward GEMM on transposed operands.  For y = x W^T (x [M, K], W [N, K]):
+ *   dX [M, K] = dY W     = mx_gemm_e5m2_e4m3(quant_e5m2(dY) [M, N], quant_transpose_e4m3(W) [K, N])
+ *   dW [N, K] = dY^T x   = mx_gemm_e5m2_e4m3(quant_transpose_e5m2(dY) [N, M],
+ *                                           quant_transpose_e4m3(x) [K, M])
+ *
+ * mx_quant_e5m2: bf16 x [M, K] -> E5M2 codes q [M, K] + E8M0 bytes s [M, K/32], per 32 along K:
+ *   E = ceil(log2(amax / 57344)) with amax floored at 2^-126 and E at -127 (byte E + 127); the
+ *   codes round x / 2^E (exact) to nearest even (stochastic == 0) or stochastically (stochastic
+ *   != 0): the larger neighbour when u < 2^32 (|y| - lo) / (hi - lo), u the 32-bit uniform of the
+ *   element, word i & 7 (64-bit word (i & 7) / 2, low half first) of Philox4x64-10 block i >> 3
+ *   under key (seed, 0), i the element's row-major index in the output (over all batches).
+ *   Same buffer rules as mx_act_quant; batched: strides as mx_act_quant_strided_batched.
+ * mx_quant_transpose_e4m3: bf16 x [R, C] -> E4M3 codes q [C, R] + E8M0 bytes s [C, R/32]: exactly
+ *   mx_act_quant of x^T, without a transposed copy.
+ * mx_quant_transpose_e5m2: bf16 x [R, C] -> mx_quant_e5m2 of x^T (codes [C, R], bytes [C, R/32]),
+ *   the element index being the code's position in the [C, R] output.
+ *   Both: R % 32 == 0 and C % 8 == 0 (MX_ERR_SHAPE), x and q 16-byte aligned (MX_ERR_ALIGN).
+ * mx_gemm_e5m2_e4m3: C = bf16_rne(A B^T) with A E5M2 [M, K] + per-row-32 E8M0 [M, K/32] and B E4M3
+ *   [N, K] + per-row-32 E8M0 [N, K/32] (the layout mx_quant_transpose_e4m3 writes), fp32
+ *   accumulation, the same accuracy bound and buffer rules as mx_gemm_fp8_fp8; decoded values must
+ *   be bf16 normals (E5M2 scale bytes >= 17).
+ * ------------------------------------------------------------------------------------------- */
+int mx_quant_e5m2(const void* x, void* q, void* s, int64_t M, int64_t K, int stochastic,
+                  uint64_t seed, void* stream);
+int mx_quant_e5m2_strided_batched(const void* x, void* q, void* s, int64_t M, int64_t K,
+                                  int64_t batch, int64_t stride_x, int64_t stride_q,
+                                  int64_t stride_s, int stochastic, uint64_t seed, void* stream);
+int mx_quant_transpose_e4m3(const void* x, void* q, void* s, int64_t R, int64_t C, void* stream);
+int mx_quant_transpose_e5m2(const void* x, void* q, void* s, int64_t R, int64_t C, int stochastic,
+                            uint64_t seed, void* stream);
+int mx_gemm_e5m2_e4m3(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                      void* c, int64_t M, int64_t N, int64_t K, void* stream);
+/* As mx_gemm_e5m2_e4m3 with K split across workgroups for shapes with few output tiles (the
+ * rules, workspace and errors of mx_gemm_fp8_fp4_splitk). */
+int mx_gemm_e5m2_e4m3_splitk(const void* a, const void* a_scale, const void* b,
+                             const void* b_scale, void* c, int64_t M, int64_t N, int64_t K,
+                             void* workspace, int64_t workspace_bytes, void* stream);
+int mx_gemm_e5m2_e4m3_strided_batched(const void* a, const void* a_scale, const void* b,
+                                      const void* b_scale, void* c, int64_t M, int64_t N,
+                                      int64_t K, int64_t batch, int64_t stride_a,
+                                      int64_t stride_a_scale, int64_t stride_b,
+                                      int64_t stride_b_scale, int64_t stride_c, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

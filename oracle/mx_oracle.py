@@ -522,11 +522,12 @@ def gelu_within(out_bits, pre, S) -> np.ndarray:
 # ----------------------------------------------------------------------------------------------
 # The hip_quant page's "FP8 Formats" table gives E5M2 as 1 sign, 5 exponent, 2 mantissa bits,
 # bias 15, max 57344, with Inf and NaN; its default rounding is round-to-nearest-even, and its
-# opt-in stochastic rounding for backward gradients rounds between the two neighbouring E5M2
-# values with probability proportional to the distance, using a stateless per-element hash of
-# (seed, element index).  It also offers quantize-plus-transpose for rank-2 tensors, and block-
-# wise E5M2 with one scale per 32 values along the last dimension; the AstrAI page routes the
-# weight and input gradients through the forward GEMM via contiguous transposes.  Readings (each
+# opt-in stochastic rounding for backward gradients picks one of the two E5M2 values around the
+# input, the nearer one more often in proportion to how near it is, with randomness that depends
+# only on a seed and the element's position (a hash, no generator state).  It also offers
+# quantize-plus-transpose for rank-2 tensors, and block-wise E5M2 with one scale per 32 values
+# along the last dimension; the AstrAI page feeds the weight and input gradients to the forward
+# GEMM through transposed copies.  Readings (each
 # is listed with the others):
 #   scale: act_quant's rule with E5M2's largest magnitude 57344: E = ceil(log2(amax / 57344))
 #       exactly, amax floored at the smallest normal float32 (a gradient block may be far
@@ -636,10 +637,13 @@ def uniform_u32(seed: int, idx) -> np.ndarray:
     """The 32-bit uniform of element index idx: word idx & 7 of Philox4x64-10 block idx >> 3
     under key (seed, 0) (64-bit output word (idx & 7) >> 1, low half first)."""
     idx = np.asarray(idx, dtype=np.uint64)
-    z = np.zeros_like(idx)
-    w = philox4x64_10((idx >> np.uint64(3), z, z, z), (np.uint64(seed), np.uint64(0)))
-    k = (idx & np.uint64(7)).astype(np.int64)
-    word = np.choose(k >> 1, w)
+    blocks, which = np.unique(idx >> np.uint64(3), return_inverse=True)   # each block once
+    z = np.zeros_like(blocks)
+    w = philox4x64_10((blocks, z, z, z), (np.uint64(seed), np.uint64(0)))
+    k = (idx & np.uint64(7)).astype(np.int64).reshape(-1)
+    which = which.reshape(-1)
+    word = np.choose(k >> 1, [wi[which] for wi in w]).reshape(idx.shape)
+    k = k.reshape(idx.shape)
     return ((word >> (np.uint64(32) * (k & 1).astype(np.uint64))) & _LO32).astype(np.uint64)
 
 

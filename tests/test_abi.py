@@ -42,8 +42,12 @@ def test_header_declares_the_full_boundary():
     for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
         assert f"mx_gemm_{k}_splitk" in names
     assert "mx_gemm_splitk_workspace_size" in names
+    for n in ("mx_quant_e5m2", "mx_quant_e5m2_strided_batched", "mx_quant_transpose_e4m3",
+              "mx_quant_transpose_e5m2", "mx_gemm_e5m2_e4m3", "mx_gemm_e5m2_e4m3_strided_batched",
+              "mx_gemm_e5m2_e4m3_splitk"):
+        assert n in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 38
+    assert len(names) == 45
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -224,6 +228,34 @@ def test_gemm_splitk_argument_errors(lib, kind):
         assert g(*base, A16, need, None) == mx.MX_ERR_DEVICE
         # a shape that is not split needs no workspace
         assert g(A16, A16, A16, A16, None, A16, 4096, 7168, 2048, None, 0, None) == mx.MX_ERR_DEVICE
+
+
+def test_backward_operand_argument_errors(lib):
+    q5 = lib.mx_quant_e5m2
+    assert q5(A16, A16, A16, 4, 48, 1, 7, None) == mx.MX_ERR_SHAPE          # K % 32
+    assert q5(None, A16, A16, 4, 64, 0, 0, None) == mx.MX_ERR_NULL
+    assert q5(A16 + 2, A16, A16, 4, 64, 0, 0, None) == mx.MX_ERR_ALIGN
+    assert q5(None, None, None, 0, 64, 1, 3, None) == mx.MX_OK              # empty
+    qb = lib.mx_quant_e5m2_strided_batched
+    assert qb(A16, A16, A16, 4, 64, 2, 256, 0, 8, 1, 1, None) == mx.MX_ERR_STRIDE
+    for name, extra in (("mx_quant_transpose_e4m3", ()), ("mx_quant_transpose_e5m2", (1, 5))):
+        f = getattr(lib, name)
+        assert f(A16, A16, A16, 48, 64, *extra, None) == mx.MX_ERR_SHAPE    # R % 32
+        assert f(A16, A16, A16, 64, 12, *extra, None) == mx.MX_ERR_SHAPE    # C % 8
+        assert f(A16, A16, None, 64, 64, *extra, None) == mx.MX_ERR_NULL
+        assert f(A16, A16 + 4, A16, 64, 64, *extra, None) == mx.MX_ERR_ALIGN
+        assert f(None, None, None, 0, 64, *extra, None) == mx.MX_OK
+        assert f(A16, A16, A16, 1 << 16, 1 << 16, *extra, None) == mx.MX_ERR_SHAPE
+    sk = lib.mx_gemm_e5m2_e4m3_splitk
+    assert sk(A16, A16, A16, A16, A16, 4096, 2048, 7168, None, 0, None) == mx.MX_ERR_WORKSPACE
+    g = lib.mx_gemm_e5m2_e4m3
+    assert g(A16, A16, A16, A16, A16, 16, 16, 40, None) == mx.MX_ERR_SHAPE
+    assert g(A16, A16, None, A16, A16, 16, 16, 64, None) == mx.MX_ERR_NULL
+    import torch
+    if not torch.cuda.is_available():
+        assert q5(A16, A16, A16, 4, 64, 1, 7, None) == mx.MX_ERR_DEVICE
+        assert g(A16, A16, A16, A16, A16, 16, 16, 64, None) == mx.MX_ERR_DEVICE
+        assert lib.mx_quant_transpose_e5m2(A16, A16, A16, 64, 64, 0, 0, None) == mx.MX_ERR_DEVICE
 
 
 @pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
