@@ -196,6 +196,21 @@ def test_gemm_epilogue_argument_errors(lib, kind):
     assert ggs(*og, 2, 1032, 32, 4096, 128, 0, 1024, None) == mx.MX_ERR_ALIGN
 
 
+def test_size_limit_is_enforced(lib):
+    # each matrix must hold fewer than 2^31 elements: 65535 x 32768 passes validation, 65536 not
+    f = lib.mx_act_quant
+    assert f(A16, A16, A16, 65536, 32768, None) == mx.MX_ERR_SHAPE
+    g = lib.mx_gemm_fp8_fp4
+    assert g(A16, A16, A16, A16, A16, 65536, 64, 32768, None) == mx.MX_ERR_SHAPE
+    assert g(A16, A16, A16, A16, A16, 64, 65536, 32768, None) == mx.MX_ERR_SHAPE
+    assert g(A16, A16, A16, A16, A16, 65536, 32768, 32, None) == mx.MX_ERR_SHAPE   # output
+    assert lib.mx_quant_transpose_e4m3(A16, A16, A16, 65536, 32768, None) == mx.MX_ERR_SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert f(A16, A16, A16, 65535, 32768, None) == mx.MX_ERR_DEVICE
+        assert g(A16, A16, A16, A16, A16, 65535, 64, 32768, None) == mx.MX_ERR_DEVICE
+
+
 def test_splitk_workspace_size_plan():
     # 256x256 tiles; two K ranges when there are 65..128 tiles and >= 80 K steps of 64;
     # workspace = per-tile counters (rounded up to 256 B) + tiles * 2 fp32 tiles.
