@@ -706,3 +706,41 @@ def decode_e5m2_rows(codes, scale_bytes) -> np.ndarray:
     v = e5m2_to_f64(codes)
     s = np.repeat(e8m0_to_f64(scale_bytes), BLOCK, axis=-1)
     return v * s
+
+
+# ----------------------------------------------------------------------------------------------
+# O8: the GEMM output quantized to MXFP4 for the next A4W4 layer (with or without GELU)
+# ----------------------------------------------------------------------------------------------
+# The fp4-gemm README page's bias + GELU epilogue emits packed FP4 with its scales, so that the
+# next projection reads it directly.  Here the output format is this library's MXFP4 activation
+# operand: y = the bf16 GEMM output (O3, or GELU of it, O6), then act_quant_fp4(y) (O5).
+
+def gemm_quant_fp4_ref(a, b, bias=None, gelu=False):
+    """(ref, S, y_bits, packed, scale_bytes): ref = sum_k a*b + bias (gelu: GELU of it) in float64,
+    S = sum_k |a*b|, y_bits = its bf16 rounding, (packed, scale_bytes) = act_quant_fp4(y_bits)."""
+    pre, S = gemm_ref(a, b, bias)
+    ref = gelu_f64(pre) if gelu else pre
+    y = f64_to_bf16_rne(ref)
+    packed, scales = act_quant_fp4(y)
+    return ref, S, y, packed, scales
+
+
+def decode_packed_fp4(packed, scale_bytes) -> np.ndarray:
+    """Packed E2M1 [..., N/2] with per-32 E8M0 bytes [..., N/32] -> float64 [..., N]."""
+    return decode_fp4_rows(packed, scale_bytes)
+
+
+def quant_fp4_output_within(packed, scale_bytes, ref, t) -> np.ndarray:
+    """Elementwise acceptance of an MXFP4-quantized GEMM output against the exact ref, given the
+    bound t that the bf16 value y the GPU quantized meets (|y - ref| <= t: the GEMM bound, or the
+    GELU bound).  MXFP4 rounding of y / 2^E (|y| / 2^E <= 6, no clamping) moves a value in [1, 6]
+    by at most a quarter of it (spacings 0.5, 1, 2 on [1, 2), [2, 4), [4, 6]) and a value below 1
+    by at most 0.25, so |q 2^E - y| <= 2^-2 |y| + 2^(E-2).  Together:
+        |q 2^E - ref| <= 2^-2 (|ref| + t) + t + 2^(E-2).
+    """
+    deq = decode_packed_fp4(packed, scale_bytes)
+    ref = np.asarray(ref, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    E = np.repeat(np.asarray(scale_bytes, dtype=np.int64) - 127, BLOCK, axis=-1)
+    bound = np.ldexp(np.abs(ref) + t, -2) + t + np.ldexp(1.0, E - 2)
+    return np.abs(deq - ref) <= bound
