@@ -421,7 +421,8 @@ def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
     report `graph_ms`, the time per launch of 20 launches captured in one HIP graph and replayed
     (launch overhead amortized), and `cold_ms`, the median time of single launches each after
     512 MB were written to evict the caches (events around the GEMM alone).  The A4W4 shapes
-    also time their residual and GELU epilogues."""
+    also time their residual and GELU epilogues, and bias + GELU written as packed MXFP4 for the
+    next A4W4 layer, fused and as GELU then the MXFP4 producer."""
     res = {}
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
@@ -497,6 +498,22 @@ def bench_others(mx, synth, torch, dev_u8, dev_bf16, stream):
                 lambda: fr(a, a_s, b, b_s, resid, c, bias=bias_t, stream=stream), 20, torch), 5)
             r["bias_gelu_ms"] = round(time_events(
                 lambda: fg(a, a_s, b, b_s, c, bias=bias_t, stream=stream), 20, torch), 5)
+            # the next A4W4 layer's operand straight from the epilogue, against GELU in bf16 then
+            # the MXFP4 producer on it
+            q = torch.empty(shape[:-1] + (w.N // 2,), dtype=torch.uint8, device="cuda")
+            qs = torch.empty(shape[:-1] + (w.N // 32,), dtype=torch.uint8, device="cuda")
+            fq = getattr(mx, f"mx_gemm_{kind}_bias_gelu_quant")
+
+            def unfused():
+                fg(a, a_s, b, b_s, c, bias=bias_t, stream=stream)
+                mx.mx_act_quant_fp4(c, q, qs, stream=stream)
+
+            for _ in range(3):
+                fq(a, a_s, b, b_s, q, qs, bias=bias_t, stream=stream)
+                unfused()
+            r["bias_gelu_quant_ms"] = round(time_events(
+                lambda: fq(a, a_s, b, b_s, q, qs, bias=bias_t, stream=stream), 20, torch), 5)
+            r["bias_gelu_then_quant_ms"] = round(time_events(unfused, 20, torch), 5)
         return r
 
     res["fp8xmxfp4_16x256x512"] = run(synth.fp8xmxfp4_16x256x512(), "fp8_fp4", latency=True)

@@ -66,10 +66,11 @@ _SIGS["mx_gemm_e5m2_e4m3"] = [_P, _P, _P, _P, _P, _I, _I, _I, _P]
 _SIGS["mx_gemm_e5m2_e4m3_splitk"] = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]
 _SIGS["mx_gemm_e5m2_e4m3_strided_batched"] = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                               _I, _P]
-for _n in ("fp8_fp4", "fp8_fp8"):
-    _SIGS[f"mx_gemm_{_n}_quant"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
-    _SIGS[f"mx_gemm_{_n}_quant_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                                    _I, _I, _I, _I, _I, _I, _I, _P]
+for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
+    for _v in ("_quant", "_bias_gelu_quant"):
+        _SIGS[f"mx_gemm_{_n}{_v}"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
+        _SIGS[f"mx_gemm_{_n}{_v}_strided_batched"] = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                                      _I, _I, _I, _I, _I, _I, _I, _P]
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -200,19 +201,22 @@ def mx_gemm_fp4_fp4(a, a_s, b, b_s, c, bias=None, stream=None):
     _gemm("fp4_fp4", a, a_s, b, b_s, c, bias, K=2 * a.shape[-1], stream=stream)
 
 
-def _gemm_quant(kind: str, a, a_s, b, b_s, q, q_s, bias=None, stream=None):
-    M, N, K = q.shape[-2], q.shape[-1], a.shape[-1]
+def _gemm_quant(kind: str, a, a_s, b, b_s, q, q_s, bias=None, stream=None, gelu=False):
+    fp4 = kind == "fp4_fp4"
+    M, K = q.shape[-2], a.shape[-1] * (2 if fp4 else 1)
+    N = q.shape[-1] * (2 if fp4 else 1)
     lib = load()
     st = _stream(stream)
+    v = "_bias_gelu_quant" if gelu else "_quant"
     if q.dim() == 2:
-        name = f"mx_gemm_{kind}_quant"
+        name = f"mx_gemm_{kind}{v}"
         r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), _ptr(q),
                                _ptr(q_s), M, N, K, st)
     else:
         B = q.shape[0]
         strides = [t.stride(0) if t.dim() == 3 else 0 for t in (a, a_s, b, b_s)]
         sbias = bias.stride(0) if (bias is not None and bias.dim() == 2) else 0
-        name = f"mx_gemm_{kind}_quant_strided_batched"
+        name = f"mx_gemm_{kind}{v}_strided_batched"
         r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), _ptr(q),
                                _ptr(q_s), M, N, K, B, *strides, sbias, q.stride(0),
                                q_s.stride(0), st)
@@ -228,6 +232,27 @@ def mx_gemm_fp8_fp4_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
 def mx_gemm_fp8_fp8_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
     """As mx_gemm_fp8_fp4_quant with b: E4M3 [(B,) N, K] and b_s: [(B,) ceil(N/32), K/32]."""
     _gemm_quant("fp8_fp8", a, a_s, b, b_s, q, q_s, bias, stream)
+
+
+def mx_gemm_fp4_fp4_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    """A4W4 GEMM whose bf16 output is written as the next A4W4 layer's operand: q packed E2M1
+    [(B,) M, N/2] and q_s E8M0 [(B,) M, N/32] (N % 32 == 0)."""
+    _gemm_quant("fp4_fp4", a, a_s, b, b_s, q, q_s, bias, stream)
+
+
+def mx_gemm_fp8_fp4_bias_gelu_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_quant with GELU applied before the bf16 rounding that is quantized."""
+    _gemm_quant("fp8_fp4", a, a_s, b, b_s, q, q_s, bias, stream, gelu=True)
+
+
+def mx_gemm_fp8_fp8_bias_gelu_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    """As mx_gemm_fp8_fp8_quant with GELU applied before the bf16 rounding that is quantized."""
+    _gemm_quant("fp8_fp8", a, a_s, b, b_s, q, q_s, bias, stream, gelu=True)
+
+
+def mx_gemm_fp4_fp4_bias_gelu_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=None):
+    """As mx_gemm_fp4_fp4_quant with GELU applied before the bf16 rounding that is quantized."""
+    _gemm_quant("fp4_fp4", a, a_s, b, b_s, q, q_s, bias, stream, gelu=True)
 
 
 def _gemm_epilogue(kind: str, epi: str, a, a_s, b, b_s, c, bias=None, residual=None,

@@ -452,8 +452,10 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
   });
 }
 
-// QUANT: instead of the bf16 output, write its per-32 E4M3 codes and E8M0 bytes (the next
-// layer's activation operand), computed from the same bf16 values with the act_quant arithmetic.
+// QUANT: instead of the bf16 output, write its per-32 codes and E8M0 bytes (the next layer's
+// activation operand), computed from the same bf16 values with the producers' arithmetic: E4M3
+// (act_quant) when A is E4M3, packed E2M1 (the MXFP4 producer) when A is E2M1, so an A4W4 layer
+// feeds the next A4W4 layer.  QUANT combines with kEpiGelu (GELU before the bf16 rounding).
 // EPI (bf16 output only): kEpiResidual adds the bf16 residual [M, N] before the rounding,
 // kEpiGelu applies GELU to (sum + bias); both take the bias pointer as optional (BIAS is true
 // for them and a null bias adds nothing).
@@ -698,10 +700,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
       const int row = m0 + trow, col = n0 + tch * 8;
       const int ch = tch ^ (((trow >> 2) & 1) << 2);
       const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
-      const QuantChunk qc = quant_chunk(v);
-      if (row < p.M && col < p.N) {
-        *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row) * p.N + col) = qc.codes;
-        if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
+      if constexpr (AF == kFp4) {
+        const QuantChunkFp4 qc = quant_chunk_fp4(v);
+        if (row < p.M && col < p.N) {
+          *reinterpret_cast<uint32_t*>(q + static_cast<int64_t>(row) * (p.N / 2) + col / 2) = qc.codes;
+          if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
+        }
+      } else {
+        const QuantChunk qc = quant_chunk(v);
+        if (row < p.M && col < p.N) {
+          *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row) * p.N + col) = qc.codes;
+          if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
+        }
       }
     }
   } else {
@@ -755,8 +765,10 @@ hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
          g.q, g.qs, g.stride_q, g.stride_qs, g.residual, g.stride_res,
          nullptr, nullptr, 1};
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
-  if constexpr (AF == kFp8) {
+  if constexpr (AF == kFp8 || AF == kFp4) {
     if (g.q) {
+      if (g.epi == kEpiGelu)
+        return launch_kernel<AF, BF, true, true, kEpiGelu, BM, BN, WM, WN>(p, grid, stream);
       return g.bias ? launch_kernel<AF, BF, true, true, kEpiPlain, BM, BN, WM, WN>(p, grid, stream)
                     : launch_kernel<AF, BF, false, true, kEpiPlain, BM, BN, WM, WN>(p, grid, stream);
     }

@@ -7,9 +7,11 @@
 // C[m,n] = bf16_rne(sum_k A[m,k] B[n,k] + bias[n]) with fp32 accumulation on the matrix cores
 // ("formats.py" page: decode_fp4 / decode_fp8_block / act_qdq give the decoded operands;
 // "AstrAI commit log" page: the bias is added in fp32 before the single bf16 rounding), or with
-// a bf16 residual added, or GELU applied, before that rounding.
+// a bf16 residual added, or GELU applied, before that rounding; or that bf16 output quantized to
+// MXFP4 for the next A4W4 layer (the "fp4-gemm README" page's GEMM that emits packed FP4).
 #include "mx_epilogue.h"
 #include "mx_internal.h"
+#include "mx_quant.h"
 
 namespace mx {
 namespace {
@@ -28,6 +30,9 @@ struct Args {
   int64_t stride_a, stride_as, stride_b, stride_bs, stride_bias, stride_c;
   const uint16_t* res;
   int64_t stride_res;
+  uint8_t* q;          // QUANT: packed E2M1 [M, N/2]
+  uint8_t* qs;         //        E8M0 [M, N/32]
+  int64_t stride_q, stride_qs;
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float v) {
@@ -54,15 +59,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-template <int MT, int W, int G, bool BIAS, int EPI>
+template <int MT, int NC, int W, int G, bool BIAS, int EPI, bool QUANT>
 __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
-  __shared__ v4f red[W][MT][64];
+  __shared__ v4f red[W][MT][NC][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int64_t bz = blockIdx.y;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NC;
   const int pitch = p.K / 2;
   const int kb_total = p.K / 32;
   const int KT = (p.K + 127) / 128;
@@ -80,20 +85,26 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
     a_off[t] = static_cast<uint32_t>(row) * pitch + 16 * g;
     as_off[t] = static_cast<uint32_t>(row) * kb_total + g;
   }
-  const int col = min(n0 + r16, p.N);
-  const uint32_t b_off = static_cast<uint32_t>(col) * pitch + 16 * g;
-  const uint32_t bs_off = static_cast<uint32_t>(col) * kb_total + g;
+  uint32_t b_off[NC], bs_off[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = min(n0 + 16 * c + r16, p.N);
+    b_off[c] = static_cast<uint32_t>(col) * pitch + 16 * g;
+    bs_off[c] = static_cast<uint32_t>(col) * kb_total + g;
+  }
 
   const int per = (KT + W - 1) / W;
   const int k_begin = min(wave * per, KT), k_end = min(k_begin + per, KT);
 
-  v4f acc[MT];
+  v4f acc[MT][NC];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[t][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int k0 = k_begin; k0 < k_end; k0 += G) {
-    uint4 av[G][MT], bv[G];
-    uint32_t asv[G][MT], bsv[G];
+    uint4 av[G][MT], bv[G][NC];
+    uint32_t asv[G][MT], bsv[G][NC];
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       const int kt = k0 + s;
@@ -106,46 +117,76 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
                                                  ra, live ? a_off[t] : 0x80000000u, kbyte, 0));
         asv[s][t] = __builtin_amdgcn_raw_buffer_load_b8(ras, live ? as_off[t] : 0x80000000u, kblk, 0);
       }
-      bv[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rb, live ? b_off : 0x80000000u, kbyte, 0));
-      bsv[s] = __builtin_amdgcn_raw_buffer_load_b8(rbs, live ? bs_off : 0x80000000u, kblk, 0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bv[s][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rb, live ? b_off[c] : 0x80000000u, kbyte, 0));
+        bsv[s][c] = __builtin_amdgcn_raw_buffer_load_b8(rbs, live ? bs_off[c] : 0x80000000u, kblk, 0);
+      }
     }
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       if (k0 + s >= k_end) break;
-      v8i b8 = {static_cast<int>(bv[s].x), static_cast<int>(bv[s].y), static_cast<int>(bv[s].z),
-                static_cast<int>(bv[s].w), 0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        v8i a8 = {static_cast<int>(av[s][t].x), static_cast<int>(av[s][t].y),
-                  static_cast<int>(av[s][t].z), static_cast<int>(av[s][t].w), 0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a8, b8, acc[t], kFp4, kFp4, 0, static_cast<int>(asv[s][t]), 0, static_cast<int>(bsv[s]));
+      for (int c = 0; c < NC; ++c) {
+        v8i b8 = {static_cast<int>(bv[s][c].x), static_cast<int>(bv[s][c].y),
+                  static_cast<int>(bv[s][c].z), static_cast<int>(bv[s][c].w), 0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          v8i a8 = {static_cast<int>(av[s][t].x), static_cast<int>(av[s][t].y),
+                    static_cast<int>(av[s][t].z), static_cast<int>(av[s][t].w), 0, 0, 0, 0};
+          acc[t][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a8, b8, acc[t][c], kFp4, kFp4, 0, static_cast<int>(asv[s][t]), 0,
+              static_cast<int>(bsv[s][c]));
+        }
       }
     }
   }
 
 #pragma unroll
-  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) red[wave][t][c][lane] = acc[t][c];
   __syncthreads();
-  // Wave w finishes row tiles t = w, w + W, ...: the partial sums are added in wave order.
-  for (int t = wave; t < MT; t += W) {
-    v4f sum = red[0][t][lane];
+  // Wave w finishes tiles (t, c) = w, w + W, ...: the partial sums are added in wave order.
+  // QUANT: the bf16 results go to a [16 MT][32] tile in LDS (over `red`, after a barrier), then
+  // each row's 32 values are quantized by the four lanes of a DPP quad.
+  uint16_t(*stage)[16 * NC] = reinterpret_cast<uint16_t(*)[16 * NC]>(&red[0][0][0][0]);
+  v4f sums[(MT * NC + W - 1) / W];
 #pragma unroll
-    for (int w = 1; w < W; ++w) sum += red[w][t][lane];
-    const int c = n0 + r16;
-    if (c < p.N) {
-      float bias = 0.0f;
-      if (BIAS && (EPI == kEpiPlain || p.bias != nullptr))
-        bias = bf16_bits_to_f32(p.bias[bz * p.stride_bias + c]);
-      uint16_t* out = p.c + bz * p.stride_c;
-      const uint16_t* res = p.res + bz * p.stride_res;
+  for (int i = 0; i < (MT * NC + W - 1) / W; ++i) {
+    const int tc = wave + i * W;
+    if (tc < MT * NC) {
+      const int t = tc / NC, c = tc % NC;
+      v4f sum = red[0][t][c][lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * t + 4 * g + r;
+      for (int w = 1; w < W; ++w) sum += red[w][t][c][lane];
+      sums[i] = sum;
+    }
+  }
+  if constexpr (QUANT) __syncthreads();      // every wave is done reading `red`
+#pragma unroll
+  for (int i = 0; i < (MT * NC + W - 1) / W; ++i) {
+    const int tc = wave + i * W;
+    if (tc >= MT * NC) continue;
+    const int t = tc / NC, c = tc % NC;
+    const int col = n0 + 16 * c + r16;
+    if (!QUANT && col >= p.N) continue;
+    float bias = 0.0f;
+    if (BIAS && (EPI == kEpiPlain || p.bias != nullptr) && col < p.N)
+      bias = bf16_bits_to_f32(p.bias[bz * p.stride_bias + col]);
+    uint16_t* out = p.c + bz * p.stride_c;
+    const uint16_t* res = p.res + bz * p.stride_res;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * t + 4 * g + r;
+      float v = sums[i][r] + bias;
+      if constexpr (QUANT) {
+        if constexpr (EPI == kEpiGelu) v = gelu_f32(v);
+        stage[row][16 * c + r16] = to_bf16(v);
+      } else {
         if (row >= p.M) continue;
-        const int64_t at = static_cast<int64_t>(row) * p.N + c;
-        float v = sum[r] + bias;
+        const int64_t at = static_cast<int64_t>(row) * p.N + col;
         // the residual may be the output itself: this thread reads it before writing it
         if constexpr (EPI == kEpiResidual) v += bf16_bits_to_f32(res[at]);
         if constexpr (EPI == kEpiGelu) v = gelu_f32(v);
@@ -153,35 +194,74 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
       }
     }
   }
+  if constexpr (QUANT) {
+    static_assert(NC == 2, "a quantized row block needs 32 columns");
+    __syncthreads();
+    const int idx = threadIdx.x;                // row idx / 4, columns 8 (idx % 4) .. + 8
+    if (idx < 16 * MT * 4) {                    // whole quads: the DPP max stays inside
+      const int row = idx >> 2, ch = idx & 3;
+      const uint4 v = *reinterpret_cast<const uint4*>(&stage[row][8 * ch]);
+      const QuantChunkFp4 qc = quant_chunk_fp4(v);
+      if (row < p.M) {
+        uint8_t* q = p.q + bz * p.stride_q;
+        uint8_t* qs = p.qs + bz * p.stride_qs;
+        *reinterpret_cast<uint32_t*>(q + static_cast<int64_t>(row) * (p.N / 2) + n0 / 2 + 4 * ch) = qc.codes;
+        if (ch == 0) qs[static_cast<int64_t>(row) * (p.N / 32) + n0 / 32] = static_cast<uint8_t>(qc.byte);
+      }
+    }
+  }
 }
 
-template <int MT, int W, int G>
+template <int MT, int NC, int W, int G>
+void launch_unquantized(const GemmProblem& g, dim3 grid, dim3 block, const Args& p,
+                        hipStream_t stream) {
+  if (g.epi == kEpiResidual)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, true, kEpiResidual, false>), grid,
+                       block, 0, stream, p);
+  else if (g.epi == kEpiGelu)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, true, kEpiGelu, false>), grid, block,
+                       0, stream, p);
+  else if (g.bias)
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, true, kEpiPlain, false>), grid,
+                       block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, false, kEpiPlain, false>), grid,
+                       block, 0, stream, p);
+}
+
+template <int MT, int NC, int W, int G, bool QUANT>
 hipError_t launch_skinny(const GemmProblem& g, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
-         g.residual, g.stride_res};
-  dim3 grid((g.N + 15) / 16, g.batch);
+         g.residual, g.stride_res, g.q, g.qs, g.stride_q, g.stride_qs};
+  dim3 grid((g.N + 16 * NC - 1) / (16 * NC), g.batch);
   const dim3 block(64 * W);
-  if (g.epi == kEpiResidual)
-    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true, kEpiResidual>), grid, block, 0,
-                       stream, p);
-  else if (g.epi == kEpiGelu)
-    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true, kEpiGelu>), grid, block, 0,
-                       stream, p);
-  else if (g.bias)
-    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, true, kEpiPlain>), grid, block, 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, W, G, false, kEpiPlain>), grid, block, 0,
-                       stream, p);
+  if constexpr (QUANT) {
+    if (g.epi == kEpiGelu)
+      hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, true, kEpiGelu, true>), grid, block,
+                         0, stream, p);
+    else if (g.bias)
+      hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, true, kEpiPlain, true>), grid,
+                         block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_fp4_skinny_kernel<MT, NC, W, G, false, kEpiPlain, true>), grid,
+                         block, 0, stream, p);
+  } else {
+    launch_unquantized<MT, NC, W, G>(g, grid, block, p, stream);
+  }
   return hipGetLastError();
 }
+
 
 template <int MT>
 hipError_t launch_skinny_mt(const GemmProblem& g, hipStream_t stream) {
   const int kt = (g.K + 127) / 128;
-  if (kt >= 32) return launch_skinny<MT, 8, 4>(g, stream);   // long K: 8 wavefronts share it
-  return launch_skinny<MT, 4, 4>(g, stream);
+  if (g.q) {   // quantized output: 32 columns per workgroup (one scale block of each row)
+    if (kt >= 32) return launch_skinny<MT, 2, 8, 4, true>(g, stream);
+    return launch_skinny<MT, 2, 4, 4, true>(g, stream);
+  }
+  if (kt >= 32) return launch_skinny<MT, 1, 8, 4, false>(g, stream);   // long K: 8 wavefronts
+  return launch_skinny<MT, 1, 4, 4, false>(g, stream);
 }
 
 }  // namespace

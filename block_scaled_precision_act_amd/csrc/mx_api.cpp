@@ -411,8 +411,36 @@ MX_GEMM_ENTRY_POINTS(fp4_fp4, mx::kFp4, mx::kFp4)
 
 MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp4, mx::kFp8, mx::kFp4)
 MX_GEMM_QUANT_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
+MX_GEMM_QUANT_ENTRY_POINTS(fp4_fp4, mx::kFp4, mx::kFp4)
 
 #undef MX_GEMM_QUANT_ENTRY_POINTS
+
+// GELU before the quantized output (bias optional).
+#define MX_GEMM_GELU_QUANT_ENTRY_POINTS(NAME, AF, BF)                                         \
+  int mx_gemm_##NAME##_bias_gelu_quant(const void* a, const void* a_s, const void* b,         \
+                                       const void* b_s, const void* bias, void* q, void* q_s, \
+                                       int64_t M, int64_t N, int64_t K, void* stream) {       \
+    return gemm_impl(with_epilogue(quantized(AF, BF, a, a_s, b, b_s, bias, q, q_s, M, N, K,   \
+                                             1, 0, 0, 0, 0, 0, 0, 0),                         \
+                                   mx::kEpiGelu, nullptr, 0),                                 \
+                     stream);                                                                 \
+  }                                                                                           \
+  int mx_gemm_##NAME##_bias_gelu_quant_strided_batched(                                       \
+      const void* a, const void* a_s, const void* b, const void* b_s, const void* bias,       \
+      void* q, void* q_s, int64_t M, int64_t N, int64_t K, int64_t batch, int64_t sa,         \
+      int64_t sas, int64_t sb, int64_t sbs, int64_t sbias, int64_t sq, int64_t sqs,           \
+      void* stream) {                                                                         \
+    return gemm_impl(with_epilogue(quantized(AF, BF, a, a_s, b, b_s, bias, q, q_s, M, N, K,   \
+                                             batch, sa, sas, sb, sbs, sbias, sq, sqs),        \
+                                   mx::kEpiGelu, nullptr, 0),                                 \
+                     stream);                                                                 \
+  }
+
+MX_GEMM_GELU_QUANT_ENTRY_POINTS(fp8_fp4, mx::kFp8, mx::kFp4)
+MX_GEMM_GELU_QUANT_ENTRY_POINTS(fp8_fp8, mx::kFp8, mx::kFp8)
+MX_GEMM_GELU_QUANT_ENTRY_POINTS(fp4_fp4, mx::kFp4, mx::kFp4)
+
+#undef MX_GEMM_GELU_QUANT_ENTRY_POINTS
 
 // The bias is optional (NULL adds nothing) in the residual and GELU entry points.
 #define MX_GEMM_EPILOGUE_ENTRY_POINTS(NAME, AF, BF)                                           \

@@ -194,8 +194,14 @@ int mx_gemm_fp4_fp4_bias_strided_batched(const void* a, const void* a_scale, con
  *   (q, q_scale) = act_quant(y)                             per 32 consecutive n of each row,
  *                                                           exactly as mx_act_quant does.
  * The result is byte-identical to mx_gemm_* followed by mx_act_quant on the bf16 output.
+ * mx_gemm_fp4_fp4_quant writes the A4W4 layer's next operand instead: packed E2M1 (q [M, N/2],
+ * low nibble first) + E8M0 from mx_act_quant_fp4 of the bf16 output, byte-identical to
+ * mx_gemm_fp4_fp4 followed by mx_act_quant_fp4.
+ * The _bias_gelu_quant forms apply GELU (as mx_gemm_*_bias_gelu does) before the bf16 rounding
+ * that is quantized, like the "fp4-gemm README" page's bias + GELU epilogue that emits packed
+ * FP4; they equal mx_gemm_*_bias_gelu followed by the producer of the kind's format.
  *   bias     bf16 [N], or NULL for no bias
- *   q        E4M3 codes [M, N] (16-byte aligned; written)
+ *   q        E4M3 codes [M, N] (E2M1 kind: packed [M, N/2]) (16-byte aligned; written)
  *   q_scale  E8M0 bytes [M, N/32] (written)
  * N must be a multiple of 32 (MX_ERR_SHAPE otherwise).  Operands, formats and the other rules as
  * for mx_gemm_fp8_fp4 / mx_gemm_fp8_fp8.  Batched: q + i*stride_q, q_scale + i*stride_q_scale
@@ -221,6 +227,49 @@ int mx_gemm_fp8_fp8_quant_strided_batched(const void* a, const void* a_scale, co
                                           int64_t stride_b, int64_t stride_b_scale,
                                           int64_t stride_bias, int64_t stride_q,
                                           int64_t stride_q_scale, void* stream);
+int mx_gemm_fp4_fp4_quant(const void* a, const void* a_scale, const void* b, const void* b_scale,
+                          const void* bias, void* q, void* q_scale, int64_t M, int64_t N,
+                          int64_t K, void* stream);
+int mx_gemm_fp4_fp4_quant_strided_batched(const void* a, const void* a_scale, const void* b,
+                                          const void* b_scale, const void* bias, void* q,
+                                          void* q_scale, int64_t M, int64_t N, int64_t K,
+                                          int64_t batch, int64_t stride_a, int64_t stride_a_scale,
+                                          int64_t stride_b, int64_t stride_b_scale,
+                                          int64_t stride_bias, int64_t stride_q,
+                                          int64_t stride_q_scale, void* stream);
+int mx_gemm_fp8_fp4_bias_gelu_quant(const void* a, const void* a_scale, const void* b,
+                                    const void* b_scale, const void* bias, void* q, void* q_scale,
+                                    int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp8_fp4_bias_gelu_quant_strided_batched(const void* a, const void* a_scale,
+                                                    const void* b, const void* b_scale,
+                                                    const void* bias, void* q, void* q_scale,
+                                                    int64_t M, int64_t N, int64_t K, int64_t batch,
+                                                    int64_t stride_a, int64_t stride_a_scale,
+                                                    int64_t stride_b, int64_t stride_b_scale,
+                                                    int64_t stride_bias, int64_t stride_q,
+                                                    int64_t stride_q_scale, void* stream);
+int mx_gemm_fp8_fp8_bias_gelu_quant(const void* a, const void* a_scale, const void* b,
+                                    const void* b_scale, const void* bias, void* q, void* q_scale,
+                                    int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp8_fp8_bias_gelu_quant_strided_batched(const void* a, const void* a_scale,
+                                                    const void* b, const void* b_scale,
+                                                    const void* bias, void* q, void* q_scale,
+                                                    int64_t M, int64_t N, int64_t K, int64_t batch,
+                                                    int64_t stride_a, int64_t stride_a_scale,
+                                                    int64_t stride_b, int64_t stride_b_scale,
+                                                    int64_t stride_bias, int64_t stride_q,
+                                                    int64_t stride_q_scale, void* stream);
+int mx_gemm_fp4_fp4_bias_gelu_quant(const void* a, const void* a_scale, const void* b,
+                                    const void* b_scale, const void* bias, void* q, void* q_scale,
+                                    int64_t M, int64_t N, int64_t K, void* stream);
+int mx_gemm_fp4_fp4_bias_gelu_quant_strided_batched(const void* a, const void* a_scale,
+                                                    const void* b, const void* b_scale,
+                                                    const void* bias, void* q, void* q_scale,
+                                                    int64_t M, int64_t N, int64_t K, int64_t batch,
+                                                    int64_t stride_a, int64_t stride_a_scale,
+                                                    int64_t stride_b, int64_t stride_b_scale,
+                                                    int64_t stride_bias, int64_t stride_q,
+                                                    int64_t stride_q_scale, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * GEMM with a residual or GELU epilogue (bf16 output).

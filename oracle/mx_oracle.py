@@ -361,19 +361,21 @@ def gemm_act_quant_ref(a, b, bias=None):
     return ref, S, y, codes, scales
 
 
-def quant_output_within(codes, scale_bytes, ref, S) -> np.ndarray:
+def quant_output_within(codes, scale_bytes, ref, S, t=None) -> np.ndarray:
     """Elementwise acceptance of a quantized GEMM output against the exact ref.
 
-    The GPU's bf16 value y satisfies the GEMM bound |y - ref| <= t with t = 2^-7 |ref| + 2^-20 S.
-    act_quant then rounds y / 2^E to E4M3 with no clamping (the scale rule keeps |y| / 2^E <=
+    The GPU's bf16 value y satisfies |y - ref| <= t: by default the GEMM bound
+    t = 2^-7 |ref| + 2^-20 S; with GELU before the rounding, the caller passes gelu_within's bound
+    (ref then being GELU of the exact sum).  act_quant then rounds y / 2^E to E4M3 with no clamping (the scale rule keeps |y| / 2^E <=
     448): a normal E4M3 value is off by at most half its spacing, 2^-4 of its magnitude, and a
     subnormal one by at most 2^-10, so |q 2^E - y| <= 2^-4 |y| + 2^(E-10).  Together:
         |q 2^E - ref| <= 2^-4 (|ref| + t) + t + 2^(E-10).
     """
     deq = act_qdq_f64(codes, scale_bytes)
     ref = np.asarray(ref, dtype=np.float64)
-    S = np.asarray(S, dtype=np.float64)
-    t = np.ldexp(np.abs(ref), -7) + np.ldexp(S, -20)
+    if t is None:
+        t = np.ldexp(np.abs(ref), -7) + np.ldexp(np.asarray(S, dtype=np.float64), -20)
+    t = np.asarray(t, dtype=np.float64)
     E = np.repeat(np.asarray(scale_bytes, dtype=np.int64) - 127, BLOCK, axis=-1)
     bound = np.ldexp(np.abs(ref) + t, -4) + t + np.ldexp(1.0, E - 10)
     return np.abs(deq - ref) <= bound
@@ -511,9 +513,15 @@ def gelu_within(out_bits, pre, S) -> np.ndarray:
     """
     out = bf16_to_f64(out_bits)
     g = gelu_f64(pre)
-    S = np.asarray(S, dtype=np.float64)
-    ok = np.abs(out - g) <= np.ldexp(np.abs(g), -7) + np.ldexp(S, -19) + np.ldexp(1.0, -126)
+    ok = np.abs(out - g) <= gelu_output_bound(g, S)
     return ok & np.isfinite(out)
+
+
+def gelu_output_bound(g, S) -> np.ndarray:
+    """The bound of gelu_within, 2^-7 |g| + 2^-19 S + 2^-126, for g = GELU of the exact sum: what
+    a GPU bf16 GELU output is within, and so the t of the quantized-output checks after GELU."""
+    g = np.asarray(g, dtype=np.float64)
+    return np.ldexp(np.abs(g), -7) + np.ldexp(np.asarray(S, dtype=np.float64), -19) + 2.0 ** -126
 
 
 # ----------------------------------------------------------------------------------------------

@@ -44,10 +44,14 @@ def test_header_declares_the_full_boundary():
     assert "mx_gemm_splitk_workspace_size" in names
     for n in ("mx_quant_e5m2", "mx_quant_e5m2_strided_batched", "mx_quant_transpose_e4m3",
               "mx_quant_transpose_e5m2", "mx_gemm_e5m2_e4m3", "mx_gemm_e5m2_e4m3_strided_batched",
-              "mx_gemm_e5m2_e4m3_splitk"):
+              "mx_gemm_e5m2_e4m3_splitk", "mx_gemm_fp4_fp4_quant",
+              "mx_gemm_fp4_fp4_quant_strided_batched"):
         assert n in names
+    for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
+        for v in ("_bias_gelu_quant", "_bias_gelu_quant_strided_batched"):
+            assert f"mx_gemm_{k}{v}" in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 45
+    assert len(names) == 53
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -153,10 +157,11 @@ def test_gemm_argument_errors(lib, kind):
         mx.MX_ERR_NULL
 
 
-@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8"])
-def test_gemm_quant_argument_errors(lib, kind):
-    g = getattr(lib, f"mx_gemm_{kind}_quant")
-    gs = getattr(lib, f"mx_gemm_{kind}_quant_strided_batched")
+@pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])
+@pytest.mark.parametrize("variant", ["_quant", "_bias_gelu_quant"])
+def test_gemm_quant_argument_errors(lib, kind, variant):
+    g = getattr(lib, f"mx_gemm_{kind}{variant}")
+    gs = getattr(lib, f"mx_gemm_{kind}{variant}_strided_batched")
     # a, a_s, b, b_s, bias (may be NULL), q, q_s, M, N, K
     ok = (A16, A16, A16, A16, None, A16, A16, 16, 64, 64)
     assert g(*ok[:7], 16, 48, 64, None) == mx.MX_ERR_SHAPE        # N not a multiple of 32

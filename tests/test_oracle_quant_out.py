@@ -117,3 +117,22 @@ def test_quant_output_within_boundary():
     one = np.ones((1, 32), dtype=np.uint8)
     assert not O.quant_output_within(one, scales, z, z).any()
     assert O.quant_output_within(np.zeros((1, 32), np.uint8), scales, z, z).all()
+
+
+def test_quant_output_within_explicit_t():
+    # ref 100, code for 112 at scale 2^0: 12 away; bound = (100 + t) / 16 + t + 2^-10 reaches 12
+    # at t = (12 - 6.25 - 2^-10) * 16 / 17 = 5.41085 (the GELU bound is passed this way).
+    scales = np.array([[127]], dtype=np.uint8)
+    ref = np.full((1, 32), 100.0)
+    codes = O.e4m3_encode_rne(np.full((1, 32), 112.0))
+    assert O.quant_output_within(codes, scales, ref, None, t=np.full((1, 32), 5.42)).all()
+    assert not O.quant_output_within(codes, scales, ref, None, t=np.full((1, 32), 5.40)).any()
+    # the default t is the GEMM bound: S = 0 gives t = 100/128, far below 5.4
+    assert not O.quant_output_within(codes, scales, ref, np.zeros((1, 32))).any()
+
+
+def test_gelu_output_bound_terms():
+    g = np.array([0.0, 128.0, 0.0, -256.0])
+    S = np.array([0.0, 0.0, 2.0 ** 19, 0.0])
+    assert np.array_equal(O.gelu_output_bound(g, S),
+                          [2.0 ** -126, 1.0 + 2.0 ** -126, 1.0 + 2.0 ** -126, 2.0 + 2.0 ** -126])
