@@ -440,7 +440,7 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
     static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       constexpr int i = m / TN, j = m % TN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j],
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i], acc[i][j],
                                                           0, 0, 0);
       static_for<m * kTasks / kM, (m + 1) * kTasks / kM>(task);
       __builtin_amdgcn_sched_barrier(0);
@@ -462,6 +462,20 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
 // SPLIT (splits == 2): workgroup b computes K range (b % 2) of tile b / 2 and stores its fp32
 // partial tile; the workgroup that arrives second at the tile's counter (no workgroup ever waits
 // for another) adds the other partial to its own and runs the epilogue.
+// LDS of one workgroup: the two operand stages, reused by the bf16 output tile of the epilogue,
+// then the tile's bias as fp32.
+template <int AF, int BF, int BM, int BN>
+constexpr int lds_tile_bytes() {
+  constexpr int stages = 2 * (BM * kRowBytes + BN * (byte_codes(BF) ? 64 : 32));
+  constexpr int tile = BM * BN * 2;
+  return stages > tile ? stages : tile;
+}
+
+template <int AF, int BF, int BM, int BN>
+constexpr int lds_bytes() {
+  return lds_tile_bytes<AF, BF, BM, BN>() + BN * 4;
+}
+
 template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT, int BM, int BN, int WM,
           int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
@@ -515,6 +529,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
   bf16x8 fa[2][TM], fb[2][TN];
+
+  // The tile's bias as fp32 in LDS, written before the prologue's barrier and read by the
+  // epilogue: its load latency is hidden behind the main loop.
+  float* const lds_bias = reinterpret_cast<float*>(lds + lds_tile_bytes<AF, BF, BM, BN>());
+  if (BIAS && (EPI == kEpiPlain || p.bias != nullptr)) {
+    for (int c = threadIdx.x; c < BN; c += NT)
+      lds_bias[c] = bf16_bits_to_f32(p.bias[bz * p.stride_bias + min(n0 + c, p.N - 1)]);
+  }
 
   // Pipeline: step k's codes are staged into LDS stage k & 1 during step k-1, piece by piece, and
   // each piece is reloaded for step k+1 right after it is staged.  Steps [k0, k0 + KT) of the
@@ -622,12 +644,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
 
   // Epilogue, staged through LDS: fp32 + bias, one bf16 rounding, written into a row-major bf16
-  // tile [BM][BN] (16-byte chunk c of row r at chunk c ^ (4 * bit 2 of r): the two row groups a
-  // wavefront writes in one pass, 4 rows apart, land in different halves of the bank space), then
-  // copied out in coalesced 16-byte row segments.
+  // tile [BM][BN], then copied out in coalesced 16-byte row segments.  The MFMA takes B as its
+  // first operand, so accumulator block (i, j) holds C^T: element 4 r4 + k of a lane is row
+  // 32 i + l32 and column 32 j + 8 r4 + 4 h + k of the wavefront tile, four consecutive
+  // columns of one row, written to LDS as one 8-byte store.  16-byte chunk c of tile row r sits
+  // at chunk c ^ tile_ch(r): the 16 rows that 16 lanes write in one pass land in 16 different
+  // 16-byte bank groups, and a row's chunks stay a permutation of themselves for the copy-out.
   __syncthreads();                       // every wavefront is done reading the operand stages
   constexpr int kTileRow = BN * 2;       // bytes of one bf16 tile row
   constexpr int kChunksPerRow = BN / 8;
+  auto tile_ch = [](int r, int c) {
+    return kChunksPerRow >= 16 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+  };
   if constexpr (EPI == kEpiResidual) {
     // The residual tile is first copied into the LDS tile in the same layout, with coalesced
     // 16-byte loads (zeros outside the matrix); each thread below reads the residual at its own
@@ -637,7 +665,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
       const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
       const int row = m0 + trow, col = n0 + tch * 8;
-      const int ch = tch ^ (((trow >> 2) & 1) << 2);
+      const int ch = tile_ch(trow, tch);
       uint4 v = {0u, 0u, 0u, 0u};
       if (row < p.M && col < p.N) {
         const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
@@ -657,31 +685,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int tcol = wn * WTN + 32 * j + l32;
-    float bias = 0.0f;
-    if (BIAS && (EPI == kEpiPlain || p.bias != nullptr)) {
-      const int col = min(n0 + tcol, p.N - 1);
-      bias = bf16_bits_to_f32(p.bias[bz * p.stride_bias + col]);
-    }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int tcol = wn * WTN + 32 * j + 8 * r4 + 4 * h;        // columns tcol .. tcol + 3
+      v4f bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (BIAS && (EPI == kEpiPlain || p.bias != nullptr))
+        bias4 = *reinterpret_cast<const v4f*>(lds_bias + tcol);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int trow = wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);   // rows trow, trow+1
-        const int ch = (tcol >> 3) ^ (((trow >> 2) & 1) << 2);
-        const uint32_t off = static_cast<uint32_t>(trow * kTileRow + ch * 16 + (tcol & 7) * 2);
-        float v0 = acc[i][j][r] + bias, v1 = acc[i][j][r + 1] + bias;
+      for (int i = 0; i < TM; ++i) {
+        const int trow = wm * WTM + 32 * i + l32;
+        const uint32_t off = static_cast<uint32_t>(trow * kTileRow + tile_ch(trow, tcol >> 3) * 16 +
+                                                   (tcol & 7) * 2);
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * r4 + k] + bias4[k];
         if constexpr (EPI == kEpiResidual) {
-          v0 += bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + off));
-          v1 += bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + off + kTileRow));
+          const uint2 r = *reinterpret_cast<const uint2*>(lds + off);
+          v[0] += bf16_bits_to_f32(r.x & 0xFFFFu);
+          v[1] += bf16_bits_to_f32(r.x >> 16);
+          v[2] += bf16_bits_to_f32(r.y & 0xFFFFu);
+          v[3] += bf16_bits_to_f32(r.y >> 16);
         } else if constexpr (EPI == kEpiGelu) {
-          v0 = gelu_f32(v0);
-          v1 = gelu_f32(v1);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = gelu_f32(v[k]);
         }
-        bf16x2 pk = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
-        const uint32_t w = pk_bits(pk);
-        *reinterpret_cast<uint16_t*>(lds + off) = static_cast<uint16_t>(w & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(lds + off + kTileRow) = static_cast<uint16_t>(w >> 16);
+        const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
+        const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+        *reinterpret_cast<uint2*>(lds + off) = uint2{pk_bits(lo), pk_bits(hi)};
       }
     }
   }
@@ -698,7 +728,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
       const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
       const int row = m0 + trow, col = n0 + tch * 8;
-      const int ch = tch ^ (((trow >> 2) & 1) << 2);
+      const int ch = tile_ch(trow, tch);
       const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
       if constexpr (AF == kFp4) {
         const QuantChunkFp4 qc = quant_chunk_fp4(v);
@@ -720,7 +750,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
       const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
       const int row = m0 + trow, col = n0 + tch * 8;
       if (row >= p.M || col >= p.N) continue;
-      const int ch = tch ^ (((trow >> 2) & 1) << 2);
+      const int ch = tile_ch(trow, tch);
       const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
       uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
       if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
@@ -736,12 +766,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   }
 }
 
-template <int AF, int BF, int BM, int BN>
-constexpr int lds_bytes() {
-  constexpr int stages = 2 * (BM * kRowBytes + BN * (byte_codes(BF) ? 64 : 32));
-  constexpr int tile = BM * BN * 2;
-  return stages > tile ? stages : tile;
-}
 
 template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN,
           bool SPLIT = false>
