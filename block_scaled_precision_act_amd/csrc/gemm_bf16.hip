@@ -746,20 +746,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     }
   } else {
     uint16_t* c = p.c + bz * p.stride_c;
-    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-      const int row = m0 + trow, col = n0 + tch * 8;
-      if (row >= p.M || col >= p.N) continue;
-      const int ch = tile_ch(trow, tch);
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
-      uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
-      if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-        *reinterpret_cast<uint4*>(dst) = v;
-      } else {
+    // A tile wholly inside an output whose rows are 16-byte aligned: every thread copies the same
+    // chunk column of rows trow0 + kRowStep * it, all LDS reads issued before the stores.
+    constexpr int kRowStep = NT / kChunksPerRow;
+    constexpr int kIters = BM / kRowStep;
+    static_assert(NT % kChunksPerRow == 0 && kRowStep % 16 == 0 && BM % kRowStep == 0,
+                  "copy-out rows keep their chunk swizzle");
+    if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
+        (reinterpret_cast<uintptr_t>(c) & 15u) == 0) {
+      const int trow0 = threadIdx.x / kChunksPerRow, tch = threadIdx.x % kChunksPerRow;
+      const uint8_t* src = lds + trow0 * kTileRow + tile_ch(trow0, tch) * 16;
+      uint4 v[kIters];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
-          if (col + k < p.N) dst[k] = static_cast<uint16_t>((k & 1) ? w >> 16 : w);
+      for (int it = 0; it < kIters; ++it)
+        v[it] = *reinterpret_cast<const uint4*>(src + it * kRowStep * kTileRow);
+      uint16_t* dst = c + static_cast<int64_t>(m0 + trow0) * p.N + n0 + tch * 8;
+      const int64_t step = static_cast<int64_t>(kRowStep) * p.N;
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) *reinterpret_cast<uint4*>(dst + it * step) = v[it];
+    } else {
+      for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+        const int row = m0 + trow, col = n0 + tch * 8;
+        if (row >= p.M || col >= p.N) continue;
+        const int ch = tile_ch(trow, tch);
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
+        uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
+        if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
+            if (col + k < p.N) dst[k] = static_cast<uint16_t>((k & 1) ? w >> 16 : w);
+          }
         }
       }
     }
