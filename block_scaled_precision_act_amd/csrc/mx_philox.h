@@ -15,6 +15,19 @@ struct Philox4x64Out {
   uint64_t w[4];
 };
 
+// The full 128-bit product a * b as (hi, lo), from four 32 x 32 -> 64-bit multiply-adds: every
+// partial sum fits in 64 bits, (2^32 - 1)^2 + 2 (2^32 - 1) = 2^64 - 1, so no carry is lost.
+__device__ __forceinline__ void mul64_full(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint64_t a0 = static_cast<uint32_t>(a), a1 = a >> 32;
+  const uint64_t b0 = static_cast<uint32_t>(b), b1 = b >> 32;
+  const uint64_t p00 = a0 * b0;
+  const uint64_t p01 = a0 * b1 + (p00 >> 32);
+  const uint64_t p10 = a1 * b0 + static_cast<uint32_t>(p01);
+  const uint64_t p11 = a1 * b1 + (p01 >> 32);
+  lo = (p10 << 32) | static_cast<uint32_t>(p00);
+  hi = p11 + (p10 >> 32);
+}
+
 // Block `ctr` (counter (ctr, 0, 0, 0)) under key (seed, 0).
 __device__ __forceinline__ Philox4x64Out philox4x64_10(uint64_t ctr, uint64_t seed) {
   constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
@@ -26,8 +39,9 @@ __device__ __forceinline__ Philox4x64Out philox4x64_10(uint64_t ctr, uint64_t se
       k0 += kW0;
       k1 += kW1;
     }
-    const uint64_t h0 = __umul64hi(kM0, x0), l0 = kM0 * x0;
-    const uint64_t h1 = __umul64hi(kM1, x2), l1 = kM1 * x2;
+    uint64_t h0, l0, h1, l1;
+    mul64_full(kM0, x0, h0, l0);
+    mul64_full(kM1, x2, h1, l1);
     x0 = h1 ^ x1 ^ k0;
     x1 = l1;
     x2 = h0 ^ x3 ^ k1;
