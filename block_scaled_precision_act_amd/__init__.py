@@ -22,9 +22,10 @@ _lib = None
 
 
 class MxError(RuntimeError):
-    def __init__(self, fn: str, status: int):
+    def __init__(self, fn: str, status: int, detail: str | None = None):
         self.status = status
-        super().__init__(f"{fn} failed: status {status} ({status_str(status)})")
+        msg = f"{fn} failed: status {status} ({status_str(status)})"
+        super().__init__(msg if detail is None else f"{msg}: {detail}")
 
 
 class MxCaps(ctypes.Structure):
@@ -116,6 +117,85 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _need(fn: str, t, what: str, dtype: str, rows: int, cols: int, batch: int | None = None,
+          output: bool = False):
+    """Checks that tensor `t` can be passed to the library as `what`: a tensor on the current GPU
+    of dtype `dtype` ("u8" or "bf16") shaped [rows, cols], or [batch, rows, cols] in a batched
+    call (an input may also be a single [rows, cols] matrix, broadcast to every batch), whose
+    rows are contiguous (column stride 1, row stride cols) as the library addresses them.  The
+    library sees only pointers, so a host tensor or a buffer smaller than this would be read or
+    written out of bounds on the GPU; such arguments raise here instead."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {what} must be a torch tensor, got {type(t).__name__}")
+    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+        raise MxError(fn, MX_ERR_DEVICE, f"{what} is on {t.device}, not the current GPU")
+    want = torch.uint8 if dtype == "u8" else torch.bfloat16
+    if t.dtype != want:
+        raise TypeError(f"{fn}: {what} must be {want}, got {t.dtype}")
+    if batch is None:
+        ok = t.dim() == 2
+    elif output:
+        ok = t.dim() == 3 and t.shape[0] == batch
+    else:
+        ok = t.dim() == 2 or (t.dim() == 3 and t.shape[0] == batch)
+    if not ok or tuple(t.shape[-2:]) != (rows, cols):
+        lead = "" if batch is None else f"{batch}, "
+        raise MxError(fn, MX_ERR_SHAPE, f"{what} has shape {tuple(t.shape)}, expected "
+                                        f"[{lead}{rows}, {cols}]")
+    if t.numel() > 0 and ((cols > 1 and t.stride(-1) != 1) or (rows > 1 and t.stride(-2) != cols)
+                          or (t.dim() == 3 and t.stride(0) < 0)):
+        raise MxError(fn, MX_ERR_STRIDE, f"{what} rows are not contiguous (strides "
+                                         f"{tuple(t.stride())})")
+
+
+def _need_bias(fn: str, bias, N: int, batch: int | None):
+    """bias: bf16 [N], or [batch, N] in a batched call (a [N] bias is shared by every batch)."""
+    if bias is None:
+        return
+    if bias.dim() == 1:
+        _need(fn, bias.unsqueeze(0), "bias", "bf16", 1, N)
+    else:
+        _need(fn, bias.unsqueeze(1), "bias", "bf16", 1, N, batch, output=True)
+
+
+def _need_workspace(fn: str, ws):
+    import torch
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or \
+            ws.device.index != torch.cuda.current_device():
+        raise MxError(fn, MX_ERR_DEVICE, "the workspace must be a tensor on the current GPU")
+    if not ws.is_contiguous():
+        raise MxError(fn, MX_ERR_STRIDE, "the workspace must be contiguous")
+
+
+# Operand shapes per GEMM kind: (A columns, B rows, B columns, B scale rows) for M, N, K.
+def _operand_shapes(kind: str, N: int, K: int):
+    a_cols = K // 2 if kind == "fp4_fp4" else K
+    b_cols = K if kind in ("fp8_fp8", "e5m2_e4m3") else K // 2
+    bs_rows = _cdiv(N, 32) if kind == "fp8_fp8" else N
+    return a_cols, b_cols, bs_rows
+
+
+def _need_operands(fn: str, kind: str, a, a_s, b, b_s, M: int, N: int, K: int,
+                   batch: int | None):
+    a_cols, b_cols, bs_rows = _operand_shapes(kind, N, K)
+    kb = _cdiv(K, 32)
+    _need(fn, a, "a", "u8", M, a_cols, batch)
+    _need(fn, a_s, "a_s", "u8", M, kb, batch)
+    _need(fn, b, "b", "u8", N, b_cols, batch)
+    _need(fn, b_s, "b_s", "u8", bs_rows, kb, batch)
+
+
+def _k_of(kind: str, a) -> int:
+    return a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+
+
 def _check(fn: str, st: int):
     if st != MX_OK:
         raise MxError(fn, st)
@@ -124,6 +204,9 @@ def _check(fn: str, st: int):
 def mx_act_quant(x, q, s, stream=None):
     """x: bf16 [M, K] (cuda); q: uint8 [M, K]; s: uint8 [M, K/32] (written)."""
     M, K = x.shape[-2], x.shape[-1]
+    _need("mx_act_quant", x, "x", "bf16", M, K)
+    _need("mx_act_quant", q, "q", "u8", M, K)
+    _need("mx_act_quant", s, "s", "u8", M, _cdiv(K, 32))
     _check("mx_act_quant", load().mx_act_quant(_ptr(x), _ptr(q), _ptr(s), M, K, _stream(stream)))
 
 
@@ -131,6 +214,10 @@ def mx_act_quant_strided_batched(x, q, s, stream=None):
     """x: bf16 [B, M, K]; q: uint8 [B, M, K]; s: uint8 [B, M, K/32]; batch strides from the
     tensors (a stride-0 x broadcasts)."""
     B, M, K = x.shape
+    fn = "mx_act_quant_strided_batched"
+    _need(fn, x, "x", "bf16", M, K, B, output=True)
+    _need(fn, q, "q", "u8", M, K, B, output=True)
+    _need(fn, s, "s", "u8", M, _cdiv(K, 32), B, output=True)
     _check("mx_act_quant_strided_batched",
            load().mx_act_quant_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
                                                x.stride(0), q.stride(0), s.stride(0),
@@ -140,6 +227,9 @@ def mx_act_quant_strided_batched(x, q, s, stream=None):
 def mx_act_quant_fp4(x, q, s, stream=None):
     """x: bf16 [M, K] (cuda); q: uint8 [M, K/2] packed E2M1; s: uint8 [M, K/32] (written)."""
     M, K = x.shape[-2], x.shape[-1]
+    _need("mx_act_quant_fp4", x, "x", "bf16", M, K)
+    _need("mx_act_quant_fp4", q, "q", "u8", M, K // 2)
+    _need("mx_act_quant_fp4", s, "s", "u8", M, _cdiv(K, 32))
     _check("mx_act_quant_fp4",
            load().mx_act_quant_fp4(_ptr(x), _ptr(q), _ptr(s), M, K, _stream(stream)))
 
@@ -147,6 +237,10 @@ def mx_act_quant_fp4(x, q, s, stream=None):
 def mx_act_quant_fp4_strided_batched(x, q, s, stream=None):
     """x: bf16 [B, M, K]; q: uint8 [B, M, K/2]; s: uint8 [B, M, K/32]; strides from the tensors."""
     B, M, K = x.shape
+    fn = "mx_act_quant_fp4_strided_batched"
+    _need(fn, x, "x", "bf16", M, K, B, output=True)
+    _need(fn, q, "q", "u8", M, K // 2, B, output=True)
+    _need(fn, s, "s", "u8", M, _cdiv(K, 32), B, output=True)
     _check("mx_act_quant_fp4_strided_batched",
            load().mx_act_quant_fp4_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
                                                    x.stride(0), q.stride(0), s.stride(0),
@@ -156,7 +250,12 @@ def mx_act_quant_fp4_strided_batched(x, q, s, stream=None):
 def _gemm(kind: str, a, a_s, b, b_s, c, bias=None, K=None, stream=None):
     M, N = c.shape[-2], c.shape[-1]
     if K is None:
-        K = a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+        K = _k_of(kind, a)
+    batch = c.shape[0] if c.dim() == 3 else None
+    fn = f"mx_gemm_{kind}"
+    _need(fn, c, "c", "bf16", M, N, batch, output=True)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch)
+    _need_bias(fn, bias, N, batch)
     lib = load()
     st = _stream(stream)
     if c.dim() == 2:
@@ -205,9 +304,15 @@ def _gemm_quant(kind: str, a, a_s, b, b_s, q, q_s, bias=None, stream=None, gelu=
     fp4 = kind == "fp4_fp4"
     M, K = q.shape[-2], a.shape[-1] * (2 if fp4 else 1)
     N = q.shape[-1] * (2 if fp4 else 1)
+    v = "_bias_gelu_quant" if gelu else "_quant"
+    batch = q.shape[0] if q.dim() == 3 else None
+    fn = f"mx_gemm_{kind}{v}"
+    _need(fn, q, "q", "u8", M, q.shape[-1], batch, output=True)
+    _need(fn, q_s, "q_s", "u8", M, _cdiv(N, 32), batch, output=True)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch)
+    _need_bias(fn, bias, N, batch)
     lib = load()
     st = _stream(stream)
-    v = "_bias_gelu_quant" if gelu else "_quant"
     if q.dim() == 2:
         name = f"mx_gemm_{kind}{v}"
         r = getattr(lib, name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias), _ptr(q),
@@ -258,7 +363,14 @@ def mx_gemm_fp4_fp4_bias_gelu_quant(a, a_s, b, b_s, q, q_s, bias=None, stream=No
 def _gemm_epilogue(kind: str, epi: str, a, a_s, b, b_s, c, bias=None, residual=None,
                    stream=None):
     M, N = c.shape[-2], c.shape[-1]
-    K = a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+    K = _k_of(kind, a)
+    batch = c.shape[0] if c.dim() == 3 else None
+    fn = f"mx_gemm_{kind}_bias_{epi}"
+    _need(fn, c, "c", "bf16", M, N, batch, output=True)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch)
+    _need_bias(fn, bias, N, batch)
+    if epi == "residual":
+        _need(fn, residual, "residual", "bf16", M, N, batch)
     lib = load()
     st = _stream(stream)
     res = [_ptr(residual)] if epi == "residual" else []
@@ -316,7 +428,12 @@ def mx_gemm_splitk_workspace_size(M: int, N: int, K: int) -> int:
 
 def _gemm_splitk(kind: str, a, a_s, b, b_s, c, workspace, bias=None, stream=None):
     M, N = c.shape
-    K = a.shape[-1] * (2 if kind == "fp4_fp4" else 1)
+    K = _k_of(kind, a)
+    fn = f"mx_gemm_{kind}_splitk"
+    _need(fn, c, "c", "bf16", M, N)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, None)
+    _need_bias(fn, bias, N, None)
+    _need_workspace(fn, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     name = f"mx_gemm_{kind}_splitk"
     _check(name, getattr(load(), name)(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(bias),
@@ -346,6 +463,11 @@ def mx_quant_e5m2(x, q, s, seed=None, stream=None):
     nearest even (seed None) or stochastically from Philox4x64-10 under `seed`."""
     st, sd = (0, 0) if seed is None else (1, int(seed))
     M, K = x.shape[-2], x.shape[-1]
+    batch = x.shape[0] if x.dim() == 3 else None
+    fn = "mx_quant_e5m2"
+    _need(fn, x, "x", "bf16", M, K, batch, output=True)
+    _need(fn, q, "q", "u8", M, K, batch, output=True)
+    _need(fn, s, "s", "u8", M, _cdiv(K, 32), batch, output=True)
     if x.dim() == 2:
         _check("mx_quant_e5m2", load().mx_quant_e5m2(_ptr(x), _ptr(q), _ptr(s), M, K, st, sd,
                                                      _stream(stream)))
@@ -359,6 +481,10 @@ def mx_quant_e5m2(x, q, s, seed=None, stream=None):
 def mx_quant_transpose_e4m3(x, q, s, stream=None):
     """x: bf16 [R, C] -> q: E4M3 [C, R], s: E8M0 [C, R/32] (act_quant of x^T)."""
     R, C = x.shape
+    fn = "mx_quant_transpose_e4m3"
+    _need(fn, x, "x", "bf16", R, C)
+    _need(fn, q, "q", "u8", C, R)
+    _need(fn, s, "s", "u8", C, _cdiv(R, 32))
     _check("mx_quant_transpose_e4m3",
            load().mx_quant_transpose_e4m3(_ptr(x), _ptr(q), _ptr(s), R, C, _stream(stream)))
 
@@ -366,6 +492,10 @@ def mx_quant_transpose_e4m3(x, q, s, stream=None):
 def mx_quant_transpose_e5m2(x, q, s, seed=None, stream=None):
     """x: bf16 [R, C] -> q: E5M2 [C, R], s: E8M0 [C, R/32] (mx_quant_e5m2 of x^T)."""
     R, C = x.shape
+    fn = "mx_quant_transpose_e5m2"
+    _need(fn, x, "x", "bf16", R, C)
+    _need(fn, q, "q", "u8", C, R)
+    _need(fn, s, "s", "u8", C, _cdiv(R, 32))
     st, sd = (0, 0) if seed is None else (1, int(seed))
     _check("mx_quant_transpose_e5m2",
            load().mx_quant_transpose_e5m2(_ptr(x), _ptr(q), _ptr(s), R, C, st, sd,
@@ -376,6 +506,10 @@ def mx_gemm_e5m2_e4m3(a, a_s, b, b_s, c, stream=None):
     """a: E5M2 [(B,) M, K] + a_s [(B,) M, K/32]; b: E4M3 [(B,) N, K] + b_s [(B,) N, K/32] (per-row
     scales); c: bf16 [(B,) M, N] = a b^T."""
     M, N, K = c.shape[-2], c.shape[-1], a.shape[-1]
+    batch = c.shape[0] if c.dim() == 3 else None
+    fn = "mx_gemm_e5m2_e4m3"
+    _need(fn, c, "c", "bf16", M, N, batch, output=True)
+    _need_operands(fn, "e5m2_e4m3", a, a_s, b, b_s, M, N, K, batch)
     lib = load()
     if c.dim() == 2:
         _check("mx_gemm_e5m2_e4m3", lib.mx_gemm_e5m2_e4m3(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
@@ -392,6 +526,10 @@ def mx_gemm_e5m2_e4m3_splitk(a, a_s, b, b_s, c, workspace, stream=None):
     """As mx_gemm_e5m2_e4m3 (single problem) with K split across workgroups for shapes with few
     output tiles; workspace as for mx_gemm_fp8_fp4_splitk (None where the shape is not split)."""
     M, N, K = c.shape[0], c.shape[1], a.shape[-1]
+    fn = "mx_gemm_e5m2_e4m3_splitk"
+    _need(fn, c, "c", "bf16", M, N)
+    _need_operands(fn, "e5m2_e4m3", a, a_s, b, b_s, M, N, K, None)
+    _need_workspace(fn, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("mx_gemm_e5m2_e4m3_splitk",
            load().mx_gemm_e5m2_e4m3_splitk(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c), M, N,
