@@ -186,7 +186,11 @@ def main():
                 "traffic": _traffic("gemm_fp8_fp4_4096x7168x2048", GEMM_SOURCES),
                 "kernel": "gemm_bf16_kernel<fp8, fp4, bias> (E4M3/E2M1 decoded exactly to bf16, "
                           "bf16 MFMA)", "avg_launch_ms": round(gemm_ms, 5),
-                "algorithmic_flops_per_launch": flops}
+                "algorithmic_flops_per_launch": flops,
+                "frac_of_fp8_peak": round(gemm_tflops / MFMA_PEAK_TFLOPS["fp8"], 4),
+                "peak_note": "peak is the bf16 MFMA's, the instruction this GEMM runs on: the FP8 "
+                             "MFMA (5.0 PF) adds mixed-exponent products inexactly and misses the "
+                             "2^-20*sum|a*b| bound; frac_of_fp8_peak is against the FP8 peak"}
 
     # ---- the same GEMM emitting the next layer's activation operand (E4M3 codes + per-32 E8M0
     # bytes of the bf16 output): the quantizing epilogue against the bf16 output followed by
