@@ -106,11 +106,23 @@ def mx_capability() -> dict:
             "reason": caps.reason.decode()}
 
 
+_RAW_STREAM = []
+
+
 def _stream(stream):
-    if stream is None:
+    """The hipStream_t to launch on: `stream` (a torch stream or a raw handle), else torch's
+    current stream on the current device (through torch's raw-handle getter where it exists,
+    which skips building a stream object: 0.06 instead of 2.7 us per call)."""
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    if not _RAW_STREAM:
         import torch
-        return torch.cuda.current_stream().cuda_stream
-    return stream if isinstance(stream, int) else stream.cuda_stream
+        _RAW_STREAM.append(getattr(torch._C, "_cuda_getCurrentRawStream", None))
+    raw = _RAW_STREAM[0]
+    if raw is not None:
+        return raw(_current_device())
+    import torch
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t):
@@ -121,46 +133,81 @@ def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
+_DT = {}
+
+
+def _dtypes():
+    if not _DT:
+        import torch
+        _DT.update(u8=torch.uint8, bf16=torch.bfloat16, tensor=torch.Tensor,
+                   current=torch.cuda.current_device)
+    return _DT
+
+
+def _current_device() -> int:
+    """The current GPU's index, or -1 when no GPU is visible (every tensor is then refused)."""
+    try:
+        return _dtypes()["current"]()
+    except Exception:
+        return -1
+
+
 def _need(fn: str, t, what: str, dtype: str, rows: int, cols: int, batch: int | None = None,
-          output: bool = False):
+          output: bool = False, dev: int | None = None):
     """Checks that tensor `t` can be passed to the library as `what`: a tensor on the current GPU
-    of dtype `dtype` ("u8" or "bf16") shaped [rows, cols], or [batch, rows, cols] in a batched
-    call (an input may also be a single [rows, cols] matrix, broadcast to every batch), whose
-    rows are contiguous (column stride 1, row stride cols) as the library addresses them.  The
-    library sees only pointers, so a host tensor or a buffer smaller than this would be read or
-    written out of bounds on the GPU; such arguments raise here instead."""
-    import torch
-    if not isinstance(t, torch.Tensor):
+    (index `dev`, queried once per call by the caller when given) of dtype `dtype` ("u8" or
+    "bf16") shaped [rows, cols], or [batch, rows, cols] in a batched call (an input may also be a
+    single [rows, cols] matrix, broadcast to every batch), whose rows are contiguous (column
+    stride 1, row stride cols) as the library addresses them.  The library sees only pointers, so
+    a host tensor or a buffer smaller than this would be read or written out of bounds on the
+    GPU; such arguments raise here instead."""
+    dt = _DT or _dtypes()
+    if not isinstance(t, dt["tensor"]):
         raise TypeError(f"{fn}: {what} must be a torch tensor, got {type(t).__name__}")
-    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+    d = t.get_device()
+    if d < 0 or d != (_current_device() if dev is None else dev):
         raise MxError(fn, MX_ERR_DEVICE, f"{what} is on {t.device}, not the current GPU")
-    want = torch.uint8 if dtype == "u8" else torch.bfloat16
-    if t.dtype != want:
-        raise TypeError(f"{fn}: {what} must be {want}, got {t.dtype}")
+    if t.dtype is not dt[dtype]:
+        raise TypeError(f"{fn}: {what} must be {dt[dtype]}, got {t.dtype}")
+    sh = t.shape
+    nd = len(sh)
     if batch is None:
-        ok = t.dim() == 2
+        ok = nd == 2
     elif output:
-        ok = t.dim() == 3 and t.shape[0] == batch
+        ok = nd == 3 and sh[0] == batch
     else:
-        ok = t.dim() == 2 or (t.dim() == 3 and t.shape[0] == batch)
-    if not ok or tuple(t.shape[-2:]) != (rows, cols):
+        ok = nd == 2 or (nd == 3 and sh[0] == batch)
+    if not ok or sh[-2] != rows or sh[-1] != cols:
         lead = "" if batch is None else f"{batch}, "
-        raise MxError(fn, MX_ERR_SHAPE, f"{what} has shape {tuple(t.shape)}, expected "
+        raise MxError(fn, MX_ERR_SHAPE, f"{what} has shape {tuple(sh)}, expected "
                                         f"[{lead}{rows}, {cols}]")
-    if t.numel() > 0 and ((cols > 1 and t.stride(-1) != 1) or (rows > 1 and t.stride(-2) != cols)
-                          or (t.dim() == 3 and t.stride(0) < 0)):
-        raise MxError(fn, MX_ERR_STRIDE, f"{what} rows are not contiguous (strides "
-                                         f"{tuple(t.stride())})")
+    if t.is_contiguous():          # rows of cols elements, one after another
+        return
+    st = t.stride()
+    if rows and cols and (cols > 1 and st[-1] != 1 or rows > 1 and st[-2] != cols or
+                          nd == 3 and st[0] < 0):
+        raise MxError(fn, MX_ERR_STRIDE, f"{what} rows are not contiguous (strides {st})")
 
 
-def _need_bias(fn: str, bias, N: int, batch: int | None):
+def _need_bias(fn: str, bias, N: int, batch: int | None, dev: int | None = None):
     """bias: bf16 [N], or [batch, N] in a batched call (a [N] bias is shared by every batch)."""
     if bias is None:
         return
-    if bias.dim() == 1:
-        _need(fn, bias.unsqueeze(0), "bias", "bf16", 1, N)
-    else:
-        _need(fn, bias.unsqueeze(1), "bias", "bf16", 1, N, batch, output=True)
+    dt = _DT or _dtypes()
+    if not isinstance(bias, dt["tensor"]):
+        raise TypeError(f"{fn}: bias must be a torch tensor, got {type(bias).__name__}")
+    d = bias.get_device()
+    if d < 0 or d != (_current_device() if dev is None else dev):
+        raise MxError(fn, MX_ERR_DEVICE, f"bias is on {bias.device}, not the current GPU")
+    if bias.dtype is not dt["bf16"]:
+        raise TypeError(f"{fn}: bias must be {dt['bf16']}, got {bias.dtype}")
+    sh = bias.shape
+    if not (len(sh) == 1 or (batch is not None and len(sh) == 2 and sh[0] == batch)) or \
+            sh[-1] != N:
+        raise MxError(fn, MX_ERR_SHAPE, f"bias has shape {tuple(sh)}, expected [{N}]" +
+                      ("" if batch is None else f" or [{batch}, {N}]"))
+    if N > 1 and bias.stride(-1) != 1 or len(sh) == 2 and bias.stride(0) < 0:
+        raise MxError(fn, MX_ERR_STRIDE, f"bias elements are not contiguous ({bias.stride()})")
 
 
 def _need_workspace(fn: str, ws):
@@ -183,13 +230,13 @@ def _operand_shapes(kind: str, N: int, K: int):
 
 
 def _need_operands(fn: str, kind: str, a, a_s, b, b_s, M: int, N: int, K: int,
-                   batch: int | None):
+                   batch: int | None, dev: int | None = None):
     a_cols, b_cols, bs_rows = _operand_shapes(kind, N, K)
     kb = _cdiv(K, 32)
-    _need(fn, a, "a", "u8", M, a_cols, batch)
-    _need(fn, a_s, "a_s", "u8", M, kb, batch)
-    _need(fn, b, "b", "u8", N, b_cols, batch)
-    _need(fn, b_s, "b_s", "u8", bs_rows, kb, batch)
+    _need(fn, a, "a", "u8", M, a_cols, batch, dev=dev)
+    _need(fn, a_s, "a_s", "u8", M, kb, batch, dev=dev)
+    _need(fn, b, "b", "u8", N, b_cols, batch, dev=dev)
+    _need(fn, b_s, "b_s", "u8", bs_rows, kb, batch, dev=dev)
 
 
 def _k_of(kind: str, a) -> int:
@@ -204,9 +251,10 @@ def _check(fn: str, st: int):
 def mx_act_quant(x, q, s, stream=None):
     """x: bf16 [M, K] (cuda); q: uint8 [M, K]; s: uint8 [M, K/32] (written)."""
     M, K = x.shape[-2], x.shape[-1]
-    _need("mx_act_quant", x, "x", "bf16", M, K)
-    _need("mx_act_quant", q, "q", "u8", M, K)
-    _need("mx_act_quant", s, "s", "u8", M, _cdiv(K, 32))
+    dev = _current_device()
+    _need("mx_act_quant", x, "x", "bf16", M, K, dev=dev)
+    _need("mx_act_quant", q, "q", "u8", M, K, dev=dev)
+    _need("mx_act_quant", s, "s", "u8", M, _cdiv(K, 32), dev=dev)
     _check("mx_act_quant", load().mx_act_quant(_ptr(x), _ptr(q), _ptr(s), M, K, _stream(stream)))
 
 
@@ -215,9 +263,10 @@ def mx_act_quant_strided_batched(x, q, s, stream=None):
     tensors (a stride-0 x broadcasts)."""
     B, M, K = x.shape
     fn = "mx_act_quant_strided_batched"
-    _need(fn, x, "x", "bf16", M, K, B, output=True)
-    _need(fn, q, "q", "u8", M, K, B, output=True)
-    _need(fn, s, "s", "u8", M, _cdiv(K, 32), B, output=True)
+    dev = _current_device()
+    _need(fn, x, "x", "bf16", M, K, B, output=True, dev=dev)
+    _need(fn, q, "q", "u8", M, K, B, output=True, dev=dev)
+    _need(fn, s, "s", "u8", M, _cdiv(K, 32), B, output=True, dev=dev)
     _check("mx_act_quant_strided_batched",
            load().mx_act_quant_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
                                                x.stride(0), q.stride(0), s.stride(0),
@@ -227,9 +276,10 @@ def mx_act_quant_strided_batched(x, q, s, stream=None):
 def mx_act_quant_fp4(x, q, s, stream=None):
     """x: bf16 [M, K] (cuda); q: uint8 [M, K/2] packed E2M1; s: uint8 [M, K/32] (written)."""
     M, K = x.shape[-2], x.shape[-1]
-    _need("mx_act_quant_fp4", x, "x", "bf16", M, K)
-    _need("mx_act_quant_fp4", q, "q", "u8", M, K // 2)
-    _need("mx_act_quant_fp4", s, "s", "u8", M, _cdiv(K, 32))
+    dev = _current_device()
+    _need("mx_act_quant_fp4", x, "x", "bf16", M, K, dev=dev)
+    _need("mx_act_quant_fp4", q, "q", "u8", M, K // 2, dev=dev)
+    _need("mx_act_quant_fp4", s, "s", "u8", M, _cdiv(K, 32), dev=dev)
     _check("mx_act_quant_fp4",
            load().mx_act_quant_fp4(_ptr(x), _ptr(q), _ptr(s), M, K, _stream(stream)))
 
@@ -238,9 +288,10 @@ def mx_act_quant_fp4_strided_batched(x, q, s, stream=None):
     """x: bf16 [B, M, K]; q: uint8 [B, M, K/2]; s: uint8 [B, M, K/32]; strides from the tensors."""
     B, M, K = x.shape
     fn = "mx_act_quant_fp4_strided_batched"
-    _need(fn, x, "x", "bf16", M, K, B, output=True)
-    _need(fn, q, "q", "u8", M, K // 2, B, output=True)
-    _need(fn, s, "s", "u8", M, _cdiv(K, 32), B, output=True)
+    dev = _current_device()
+    _need(fn, x, "x", "bf16", M, K, B, output=True, dev=dev)
+    _need(fn, q, "q", "u8", M, K // 2, B, output=True, dev=dev)
+    _need(fn, s, "s", "u8", M, _cdiv(K, 32), B, output=True, dev=dev)
     _check("mx_act_quant_fp4_strided_batched",
            load().mx_act_quant_fp4_strided_batched(_ptr(x), _ptr(q), _ptr(s), M, K, B,
                                                    x.stride(0), q.stride(0), s.stride(0),
@@ -253,9 +304,10 @@ def _gemm(kind: str, a, a_s, b, b_s, c, bias=None, K=None, stream=None):
         K = _k_of(kind, a)
     batch = c.shape[0] if c.dim() == 3 else None
     fn = f"mx_gemm_{kind}"
-    _need(fn, c, "c", "bf16", M, N, batch, output=True)
-    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch)
-    _need_bias(fn, bias, N, batch)
+    dev = _current_device()
+    _need(fn, c, "c", "bf16", M, N, batch, output=True, dev=dev)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch, dev=dev)
+    _need_bias(fn, bias, N, batch, dev=dev)
     lib = load()
     st = _stream(stream)
     if c.dim() == 2:
@@ -307,10 +359,11 @@ def _gemm_quant(kind: str, a, a_s, b, b_s, q, q_s, bias=None, stream=None, gelu=
     v = "_bias_gelu_quant" if gelu else "_quant"
     batch = q.shape[0] if q.dim() == 3 else None
     fn = f"mx_gemm_{kind}{v}"
-    _need(fn, q, "q", "u8", M, q.shape[-1], batch, output=True)
-    _need(fn, q_s, "q_s", "u8", M, _cdiv(N, 32), batch, output=True)
-    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch)
-    _need_bias(fn, bias, N, batch)
+    dev = _current_device()
+    _need(fn, q, "q", "u8", M, q.shape[-1], batch, output=True, dev=dev)
+    _need(fn, q_s, "q_s", "u8", M, _cdiv(N, 32), batch, output=True, dev=dev)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch, dev=dev)
+    _need_bias(fn, bias, N, batch, dev=dev)
     lib = load()
     st = _stream(stream)
     if q.dim() == 2:
@@ -366,11 +419,12 @@ def _gemm_epilogue(kind: str, epi: str, a, a_s, b, b_s, c, bias=None, residual=N
     K = _k_of(kind, a)
     batch = c.shape[0] if c.dim() == 3 else None
     fn = f"mx_gemm_{kind}_bias_{epi}"
-    _need(fn, c, "c", "bf16", M, N, batch, output=True)
-    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch)
-    _need_bias(fn, bias, N, batch)
+    dev = _current_device()
+    _need(fn, c, "c", "bf16", M, N, batch, output=True, dev=dev)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, batch, dev=dev)
+    _need_bias(fn, bias, N, batch, dev=dev)
     if epi == "residual":
-        _need(fn, residual, "residual", "bf16", M, N, batch)
+        _need(fn, residual, "residual", "bf16", M, N, batch, dev=dev)
     lib = load()
     st = _stream(stream)
     res = [_ptr(residual)] if epi == "residual" else []
@@ -430,9 +484,10 @@ def _gemm_splitk(kind: str, a, a_s, b, b_s, c, workspace, bias=None, stream=None
     M, N = c.shape
     K = _k_of(kind, a)
     fn = f"mx_gemm_{kind}_splitk"
-    _need(fn, c, "c", "bf16", M, N)
-    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, None)
-    _need_bias(fn, bias, N, None)
+    dev = _current_device()
+    _need(fn, c, "c", "bf16", M, N, dev=dev)
+    _need_operands(fn, kind, a, a_s, b, b_s, M, N, K, None, dev=dev)
+    _need_bias(fn, bias, N, None, dev=dev)
     _need_workspace(fn, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     name = f"mx_gemm_{kind}_splitk"
@@ -465,9 +520,10 @@ def mx_quant_e5m2(x, q, s, seed=None, stream=None):
     M, K = x.shape[-2], x.shape[-1]
     batch = x.shape[0] if x.dim() == 3 else None
     fn = "mx_quant_e5m2"
-    _need(fn, x, "x", "bf16", M, K, batch, output=True)
-    _need(fn, q, "q", "u8", M, K, batch, output=True)
-    _need(fn, s, "s", "u8", M, _cdiv(K, 32), batch, output=True)
+    dev = _current_device()
+    _need(fn, x, "x", "bf16", M, K, batch, output=True, dev=dev)
+    _need(fn, q, "q", "u8", M, K, batch, output=True, dev=dev)
+    _need(fn, s, "s", "u8", M, _cdiv(K, 32), batch, output=True, dev=dev)
     if x.dim() == 2:
         _check("mx_quant_e5m2", load().mx_quant_e5m2(_ptr(x), _ptr(q), _ptr(s), M, K, st, sd,
                                                      _stream(stream)))
@@ -482,9 +538,10 @@ def mx_quant_transpose_e4m3(x, q, s, stream=None):
     """x: bf16 [R, C] -> q: E4M3 [C, R], s: E8M0 [C, R/32] (act_quant of x^T)."""
     R, C = x.shape
     fn = "mx_quant_transpose_e4m3"
-    _need(fn, x, "x", "bf16", R, C)
-    _need(fn, q, "q", "u8", C, R)
-    _need(fn, s, "s", "u8", C, _cdiv(R, 32))
+    dev = _current_device()
+    _need(fn, x, "x", "bf16", R, C, dev=dev)
+    _need(fn, q, "q", "u8", C, R, dev=dev)
+    _need(fn, s, "s", "u8", C, _cdiv(R, 32), dev=dev)
     _check("mx_quant_transpose_e4m3",
            load().mx_quant_transpose_e4m3(_ptr(x), _ptr(q), _ptr(s), R, C, _stream(stream)))
 
@@ -493,9 +550,10 @@ def mx_quant_transpose_e5m2(x, q, s, seed=None, stream=None):
     """x: bf16 [R, C] -> q: E5M2 [C, R], s: E8M0 [C, R/32] (mx_quant_e5m2 of x^T)."""
     R, C = x.shape
     fn = "mx_quant_transpose_e5m2"
-    _need(fn, x, "x", "bf16", R, C)
-    _need(fn, q, "q", "u8", C, R)
-    _need(fn, s, "s", "u8", C, _cdiv(R, 32))
+    dev = _current_device()
+    _need(fn, x, "x", "bf16", R, C, dev=dev)
+    _need(fn, q, "q", "u8", C, R, dev=dev)
+    _need(fn, s, "s", "u8", C, _cdiv(R, 32), dev=dev)
     st, sd = (0, 0) if seed is None else (1, int(seed))
     _check("mx_quant_transpose_e5m2",
            load().mx_quant_transpose_e5m2(_ptr(x), _ptr(q), _ptr(s), R, C, st, sd,
@@ -508,8 +566,9 @@ def mx_gemm_e5m2_e4m3(a, a_s, b, b_s, c, stream=None):
     M, N, K = c.shape[-2], c.shape[-1], a.shape[-1]
     batch = c.shape[0] if c.dim() == 3 else None
     fn = "mx_gemm_e5m2_e4m3"
-    _need(fn, c, "c", "bf16", M, N, batch, output=True)
-    _need_operands(fn, "e5m2_e4m3", a, a_s, b, b_s, M, N, K, batch)
+    dev = _current_device()
+    _need(fn, c, "c", "bf16", M, N, batch, output=True, dev=dev)
+    _need_operands(fn, "e5m2_e4m3", a, a_s, b, b_s, M, N, K, batch, dev=dev)
     lib = load()
     if c.dim() == 2:
         _check("mx_gemm_e5m2_e4m3", lib.mx_gemm_e5m2_e4m3(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
@@ -527,8 +586,9 @@ def mx_gemm_e5m2_e4m3_splitk(a, a_s, b, b_s, c, workspace, stream=None):
     output tiles; workspace as for mx_gemm_fp8_fp4_splitk (None where the shape is not split)."""
     M, N, K = c.shape[0], c.shape[1], a.shape[-1]
     fn = "mx_gemm_e5m2_e4m3_splitk"
-    _need(fn, c, "c", "bf16", M, N)
-    _need_operands(fn, "e5m2_e4m3", a, a_s, b, b_s, M, N, K, None)
+    dev = _current_device()
+    _need(fn, c, "c", "bf16", M, N, dev=dev)
+    _need_operands(fn, "e5m2_e4m3", a, a_s, b, b_s, M, N, K, None, dev=dev)
     _need_workspace(fn, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("mx_gemm_e5m2_e4m3_splitk",

@@ -63,7 +63,9 @@ template <int MT, int NC, int W, int G, bool BIAS, int EPI, bool QUANT>
 __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
   __shared__ v4f red[W][MT][NC][64];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Uniform in the compiler's view too: the per-step buffer offsets derived from it go in
+  // scalar registers (no per-lane loop around every load).
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int64_t bz = blockIdx.y;
@@ -124,9 +126,11 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
         bsv[s][c] = __builtin_amdgcn_raw_buffer_load_b8(rbs, live ? bs_off[c] : 0x80000000u, kblk, 0);
       }
     }
+    // Straight-line: a step past this wavefront's range was loaded as zeros (codes and scale
+    // bytes read past the buffer bound), so its MFMAs add +0 to accumulators that start at +0 and
+    // change nothing, and all G steps' loads stay in flight together.
 #pragma unroll
     for (int s = 0; s < G; ++s) {
-      if (k0 + s >= k_end) break;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         v8i b8 = {static_cast<int>(bv[s][c].x), static_cast<int>(bv[s][c].y),

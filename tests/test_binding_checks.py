@@ -111,3 +111,11 @@ class TestOnGpu:
         c = torch.zeros((2, M, N), dtype=torch.bfloat16, device="cuda")
         mx.mx_gemm_fp8_fp8(a, a_s, b, b_s, c)                 # broadcast B: runs
         torch.cuda.synchronize()
+
+    def test_default_stream_is_torchs_current_stream(self, mx):
+        assert mx._stream(None) == torch.cuda.current_stream().cuda_stream
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            assert mx._stream(None) == s.cuda_stream
+            assert mx._stream(None) == torch.cuda.current_stream().cuda_stream
+        assert mx._stream(s) == s.cuda_stream
