@@ -104,31 +104,82 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[t][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // With K % 128 == 0 a row's scale bytes for the G = 4 steps of a group are 16 consecutive,
+  // 4-byte aligned bytes (4 K-blocks per step): one 16-byte load per row fetches them (for a
+  // group inside K; the last group of a range may need the one-byte loads), and the
+  // lane takes byte 4 s + g of it, a quarter of the load instructions of one byte per lane and
+  // step (the loop is bound by the CUs' address-processing rate at the skinny shapes).  A scale
+  // byte outside a live step is replaced by 0 (2^-127 times zero codes: nothing), never another
+  // row's byte, which could be the E8M0 NaN 0xFF.
+  static_assert(G == 4, "16 scale bytes per group");
+  const bool vec_scales = (kb_total & 3) == 0;
   for (int k0 = k_begin; k0 < k_end; k0 += G) {
     uint4 av[G][MT], bv[G][NC];
     uint32_t asv[G][MT], bsv[G][NC];
+    // every 16-byte row read stays inside that row (rows past M are wholly out of range)
+    if (vec_scales && (k0 + G) * 4 <= kb_total) {
+      uint4 asq[MT], bsq[NC];
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        asq[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ras, as_off[t] - g, static_cast<uint32_t>(k0) * 4, 0));
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        bsq[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rbs, bs_off[c] - g, static_cast<uint32_t>(k0) * 4, 0));
+#pragma unroll
+      for (int s = 0; s < G; ++s) {
+        const int kt = k0 + s;
+        const bool live = kt < k_end && kt * 4 + g < kb_total;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint32_t d = s == 0 ? asq[t].x : s == 1 ? asq[t].y : s == 2 ? asq[t].z : asq[t].w;
+          asv[s][t] = live ? __builtin_amdgcn_ubfe(d, 8 * g, 8) : 0u;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint32_t d = s == 0 ? bsq[c].x : s == 1 ? bsq[c].y : s == 2 ? bsq[c].z : bsq[c].w;
+          bsv[s][c] = live ? __builtin_amdgcn_ubfe(d, 8 * g, 8) : 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < G; ++s) {
+        const int kt = k0 + s;
+        const bool live = kt < k_end && kt * 4 + g < kb_total;
+        const uint32_t kblk = static_cast<uint32_t>(kt) * 4;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          asv[s][t] = __builtin_amdgcn_raw_buffer_load_b8(ras, live ? as_off[t] : 0x80000000u, kblk, 0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          bsv[s][c] = __builtin_amdgcn_raw_buffer_load_b8(rbs, live ? bs_off[c] : 0x80000000u, kblk, 0);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       const int kt = k0 + s;
       const bool live = kt < k_end && kt * 4 + g < kb_total;
       const uint32_t kbyte = static_cast<uint32_t>(kt) * 64;     // 128 codes = 64 bytes per row
-      const uint32_t kblk = static_cast<uint32_t>(kt) * 4;
+      if (kt < k_end) {         // wave-uniform: a step past the range issues no loads
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        av[s][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 ra, live ? a_off[t] : 0x80000000u, kbyte, 0));
-        asv[s][t] = __builtin_amdgcn_raw_buffer_load_b8(ras, live ? as_off[t] : 0x80000000u, kblk, 0);
-      }
+        for (int t = 0; t < MT; ++t)
+          av[s][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   ra, live ? a_off[t] : 0x80000000u, kbyte, 0));
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        bv[s][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rb, live ? b_off[c] : 0x80000000u, kbyte, 0));
-        bsv[s][c] = __builtin_amdgcn_raw_buffer_load_b8(rbs, live ? bs_off[c] : 0x80000000u, kblk, 0);
+        for (int c = 0; c < NC; ++c)
+          bv[s][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rb, live ? b_off[c] : 0x80000000u, kbyte, 0));
+      } else {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) av[s][t] = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) bv[s][c] = uint4{0u, 0u, 0u, 0u};
       }
     }
-    // Straight-line: a step past this wavefront's range was loaded as zeros (codes and scale
-    // bytes read past the buffer bound), so its MFMAs add +0 to accumulators that start at +0 and
-    // change nothing, and all G steps' loads stay in flight together.
+    // Straight-line: a step past this wavefront's range has zero codes and zero scale bytes, so
+    // its MFMAs add +0 to accumulators that start at +0 and change nothing, and all G steps'
+    // loads stay in flight together.
 #pragma unroll
     for (int s = 0; s < G; ++s) {
 #pragma unroll

@@ -358,13 +358,14 @@ int mx_gemm_fp4_fp4_bias_gelu_strided_batched(const void* a, const void* a_scale
  *
  * The "fp4-gemm README" page offers stream-K variants of its GEMM, selected only for validated
  * large down-projection shapes (API list; the paragraph after the schedule variants).  Here the
- * load-balancing variant splits K: when an M x N problem has fewer 256 x 256 output tiles than
- * the 256 CUs of an MI355X, each tile's K is cut into 2..4 equal ranges (at least 16 steps of 64
- * each) computed by separate workgroups; each stores its fp32 partial tile in the workspace, and
- * the workgroup that finishes a tile last adds the partials in range order (the same order on
- * every run, so results are reproducible), adds the bias and rounds once to bf16.  No workgroup
- * waits for another.  Shapes the plan does not split run exactly as mx_gemm_<kind>_bias (or
- * without bias) do, and need no workspace.
+ * load-balancing variant splits K: a single problem with 65..128 output tiles of 256 x 256
+ * (fewer than the 256 CUs of an MI355X) and at least 80 K steps of 64 has each tile's K cut into
+ * 2 equal ranges computed by separate workgroups; each stores its fp32 partial tile in the
+ * workspace, and the workgroup that finishes a tile last adds the partials in range order (the
+ * same order on every run, so results are reproducible), adds the bias and rounds once to bf16.
+ * No workgroup waits for another.  Shapes the plan does not split (the skinny MXFP4 x MXFP4
+ * shapes, M <= 64, among them) run exactly as mx_gemm_<kind>_bias (or without bias) do, and
+ * need no workspace.
  *
  * mx_gemm_splitk_workspace_size: bytes of workspace an M x N x K call needs; 0 when that shape is
  *   not split (also for invalid sizes).  It depends on the shape alone (safe without a GPU).

@@ -230,6 +230,7 @@ def test_splitk_workspace_size_plan():
     assert mx.mx_gemm_splitk_workspace_size(4096, 7168, 2048) == 0        # 448 tiles
     assert mx.mx_gemm_splitk_workspace_size(64, 64, 48) == 0              # invalid K
     assert mx.mx_gemm_splitk_workspace_size(-1, 64, 2048) == 0
+    assert mx.mx_gemm_splitk_workspace_size(41, 1536, 6144) == 0        # 6 tiles
 
 
 @pytest.mark.parametrize("kind", ["fp8_fp4", "fp8_fp8", "fp4_fp4"])

@@ -149,3 +149,12 @@ def test_split_shape_without_workspace_is_refused(mx):
     with pytest.raises(mx.MxError) as e:
         _run(mx, "fp8_fp4", a, a_s, w, None, 1280, 3328)
     assert e.value.status == mx.MX_ERR_WORKSPACE
+
+
+def test_skinny_fp4_shape_needs_no_workspace(mx):
+    # the skinny MXFP4 x MXFP4 kernel (M <= 64) is not split: the _splitk entry runs it as is
+    M, N, K = 41, 1536, 6144
+    assert mx.mx_gemm_splitk_workspace_size(M, N, K) == 0
+    w, a, a_s, A, B = _operands("fp4_fp4", M, N, K, seed=4, with_bias=True)
+    note("gemm splitk skinny shape, no workspace")
+    _check_full(_run(mx, "fp4_fp4", a, a_s, w, None, M, N), A, B, w)
