@@ -86,25 +86,33 @@ def time_events(fn, iters, torch):
     return start.elapsed_time(end) / iters   # ms
 
 
-def cpu_baseline(w, rows: int):
-    """The oracle as it stands on the first `rows` rows of A (all of N and K)."""
+def cpu_baseline(w, rows: int, min_seconds: float = 10.0, max_runs: int = 30):
+    """The oracle as it stands on the first `rows` rows of A (all of N and K), run again on the
+    same sample until `min_seconds` of CPU work have accumulated (at least once, at most
+    `max_runs` times); the rate is the mean over the runs."""
     from oracle import mx_oracle as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    codes, sb = O.act_quant(w.x[:rows])
-    A = O.decode_e4m3_rows(codes, sb)
-    B = O.decode_fp4_rows(w.b, w.b_s)
-    ref, S = O.gemm_ref(A, B, O.bf16_to_f64(w.bias))
-    dt = time.perf_counter() - t0
+    runs, total = 0, 0.0
+    while runs < max_runs and (runs == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        codes, sb = O.act_quant(w.x[:rows])
+        A = O.decode_e4m3_rows(codes, sb)
+        B = O.decode_fp4_rows(w.b, w.b_s)
+        ref, S = O.gemm_ref(A, B, O.bf16_to_f64(w.bias))
+        total += time.perf_counter() - t0
+        runs += 1
+        del codes, sb, A, B, ref, S
+    dt = total / runs
     flops = 2.0 * rows * w.N * w.K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "runs": runs,
             "sample": f"act_quant + decode + float64 GEMM (with sum|a*b|) for rows 0..{rows - 1} of "
-                      f"A [4096, 2048] against all 7168 weight rows; flops counted as 2*{rows}*N*K"}
+                      f"A [4096, 2048] against all 7168 weight rows, repeated {runs} times "
+                      f"({total:.1f} s in all); flops counted as 2*{rows}*N*K per run"}
 
 
 def main():
