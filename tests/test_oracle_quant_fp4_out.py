@@ -83,7 +83,7 @@ def test_quant_fp4_output_within_boundary():
 
 
 def test_quant_fp4_output_within_uses_each_blocks_scale():
-    # two blocks of one row with scales 2^0 and 2^4: a value in block 1 is judged on its own scale
+    # two blocks of one row with scales 2^0 and 2^4: a value in block 1 is checked against its own scale
     packed = np.zeros((1, 32), np.uint8)
     sb = np.array([[127, 131]], np.uint8)
     ref = np.zeros((1, 64))
