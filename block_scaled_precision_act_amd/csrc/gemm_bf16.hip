@@ -2,7 +2,7 @@
 // MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulation, fused fp32 bias, one bf16 rounding.
 //
 // What is computed ("formats.py" page: decode_fp4 / decode_fp8_block / act_qdq; "AstrAI commit
-// log" page: bias added in fp32 before the single bf16 rounding):
+// log" page: the bias joins the fp32 sum, which is then rounded to bf16 once):
 //   C[m,n] = bf16_rne( sum_k A[m,k] B[n,k] + bias[n] ),  A, B the exactly decoded operands.
 //
 // Why bf16 and not the scaled FP8 MFMA: on gfx950 the FP8 (E4M3) matrix instructions align the

@@ -6,7 +6,7 @@
 //
 // C[m,n] = bf16_rne(sum_k A[m,k] B[n,k] + bias[n]) with fp32 accumulation on the matrix cores
 // ("formats.py" page: decode_fp4 / decode_fp8_block / act_qdq give the decoded operands;
-// "AstrAI commit log" page: the bias is added in fp32 before the single bf16 rounding), or with
+// "AstrAI commit log" page: the bias joins the fp32 sum, which is rounded to bf16 once), or with
 // a bf16 residual added, or GELU applied, before that rounding; or that bf16 output quantized to
 // MXFP4 for the next A4W4 layer (the "fp4-gemm README" page's GEMM that emits packed FP4).
 #include "mx_epilogue.h"

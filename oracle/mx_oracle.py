@@ -12,8 +12,8 @@ Everything here is written to be read against the pages it follows, not to be fa
 * "hip_quant PKG-INFO" page: "FP8 Formats" table (E4M3 = 1 sign, 4 exponent, 3 mantissa bits,
   bias 7, max 448, NaN only, round to nearest even) and the BF16 checkpoint helper section
   (bf16 -> fp32 is exact from the raw bits).
-* "AstrAI commit log" page: the fused-bias commit (bias added in fp32 before the single bf16
-  rounding of the GEMM output).
+* "AstrAI commit log" page: the fused-bias commit (the bias joins the fp32 sum, and the GEMM
+  output is rounded to bf16 once).
 * "fp4-gemm README" page: the epilogue that emits the next projection's quantized input (O4: the
   bf16 GEMM output quantized with act_quant), the MXFP4 operand produced from activations (O5)
   and the bias + residual and bias + GELU epilogues (O6).
@@ -31,7 +31,7 @@ Readings taken where the pages are silent (each is listed in the design notes as
   accepted when |out - ref| <= 2^-7 |ref| + 2^-20 sum_k |a*b|.
 * Non-finite activations, NaN E4M3 codes (0x7F, 0xFF) and the NaN scale byte 255 are refused.
 * The MXFP4 producer uses act_quant's rule with E2M1's largest magnitude 6 (O5).
-* The residual is added before the single bf16 rounding, like the bias; GELU is the exact
+* The residual is added before the one rounding to bf16, like the bias; GELU is the exact
   x * Phi(x) of (sum + bias) (O6).
 
 No function here is "parity unpinned" except the GEMM below the stated tolerance (the bf16 output
@@ -213,9 +213,9 @@ def act_scale_bytes(x_bits) -> np.ndarray:
     K must be a multiple of 32; non-finite activations are refused.
     """
     x = bf16_to_f64(x_bits).astype(np.float32)   # exact: bf16 values are float32 values
-    K = x.shape[-1]
-    if K % BLOCK:
-        raise OracleRefusal(f"act_quant: last dim {K} not a multiple of {BLOCK}")
+    *lead, K = x.shape
+    if K % BLOCK != 0:
+        raise OracleRefusal(f"act_quant: the last dimension {K} is not divisible by {BLOCK}")
     if not np.all(np.isfinite(x)):
         raise OracleRefusal("act_quant: non-finite activation")
     xb = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK))
@@ -435,7 +435,7 @@ def act_scale_fp4_bytes(x_bits) -> np.ndarray:
     x = bf16_to_f64(x_bits).astype(np.float32)
     K = x.shape[-1]
     if K % BLOCK:
-        raise OracleRefusal(f"act_quant_fp4: last dim {K} not a multiple of {BLOCK}")
+        raise OracleRefusal(f"act_quant_fp4: the last dimension {K} is not divisible by {BLOCK}")
     if not np.all(np.isfinite(x)):
         raise OracleRefusal("act_quant_fp4: non-finite activation")
     xb = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK))
@@ -486,7 +486,7 @@ def gelu_f64(x) -> np.ndarray:
 def gemm_residual_ref(a, b, bias=None, residual_bits=None) -> tuple[np.ndarray, np.ndarray]:
     """(ref, S): gemm_ref with the bf16 residual [..., M, N] added to the unrounded value.
 
-    The residual enters like the bias, before the single bf16 rounding, so the GEMM acceptance
+    The residual enters like the bias, before the one rounding to bf16, so the GEMM acceptance
     bound applies unchanged to out against this ref.
     """
     ref, S = gemm_ref(a, b, bias)
@@ -593,7 +593,7 @@ def grad_scale_bytes(x_bits) -> np.ndarray:
     x = bf16_to_f64(x_bits).astype(np.float32)
     K = x.shape[-1]
     if K % BLOCK:
-        raise OracleRefusal(f"gradient quantizer: last dim {K} not a multiple of {BLOCK}")
+        raise OracleRefusal(f"gradient quantizer: the last dimension {K} is not divisible by {BLOCK}")
     if not np.all(np.isfinite(x)):
         raise OracleRefusal("gradient quantizer: non-finite value")
     xb = x.reshape(x.shape[:-1] + (K // BLOCK, BLOCK))
