@@ -225,3 +225,26 @@ def test_repeat_deterministic(mx):
     outs = [run(mx, "fp8_fp8", a, a_s, w.b, w.b_s, w.bias, w.M, w.N) for _ in range(5)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("kind,a_kind,b_kind", [("fp8_fp4", "acts", "fp4"), ("fp8_fp8", "acts", "fp8"),
+                                                ("fp4_fp4", "fp4", "fp4")])
+def test_output_with_unaligned_base_matches_aligned(mx, kind, a_kind, b_kind):
+    # C needs no alignment: an output starting 2 bytes past a 16-byte boundary takes the
+    # copy-out's per-chunk path and must hold exactly the bytes the aligned output gets from the
+    # 16-byte-store path (same kernel, same sums).  M = 512 > 64 runs the tiled kernel for every
+    # kind, with whole 256x256 tiles.
+    M, N, K = 512, 512, 256
+    w = synth.gemm_inputs(a_kind, b_kind, M, N, K, seed=77, with_bias=True)
+    a, a_s, _, A, B, bias = operands(w)
+    note(f"gemm {kind} unaligned output base")
+    aligned = run(mx, kind, a, a_s, w.b, w.b_s, w.bias, M, N)
+    big = torch.full((M * N + 8,), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    c = big[1:1 + M * N].view(M, N)
+    assert c.data_ptr() % 16 == 2
+    getattr(mx, f"mx_gemm_{kind}")(dev_u8(a), dev_u8(a_s), dev_u8(w.b), dev_u8(w.b_s), c,
+                                   bias=dev_bf16(w.bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(c), aligned)
+    assert int(big[0].view(torch.int16)) == -1 and int(big[-1].view(torch.int16)) == -1
+    assert_within(aligned, *O.gemm_ref(A, B, bias))
