@@ -106,3 +106,65 @@ def test_graph_replays_match_eager_and_oracle(mx):
     for k in eager:
         assert np.array_equal(again[k], eager[k]), k
     del g
+
+
+def test_graph_replays_splitk_quant_epilogue_and_stochastic_quantizers(mx):
+    # Split-K leaves its counters at zero after every launch, so a captured split GEMM replays
+    # with the same workspace; the quantizing epilogue and the seeded stochastic quantizers are
+    # deterministic too.  Each replay must give the eager bytes.
+    M, N, K = 1280, 3328, 5120                          # 65 tiles: the split plan cuts K in two
+    w = synth.gemm_inputs("fp8", "fp4", M, N, K, seed=91, with_bias=True)
+    wsz = mx.mx_gemm_splitk_workspace_size(M, N, K)
+    assert wsz > 0
+    rng = synth.rng_for(92)
+    g_host = synth.bf16_normal(rng, (256, 1024), std=1e-3)
+    d = dict(a=dev_u8(w.a), a_s=dev_u8(w.a_s), b=dev_u8(w.b), b_s=dev_u8(w.b_s),
+             bias=dev_bf16(w.bias), ws=torch.zeros(wsz, dtype=torch.uint8, device="cuda"),
+             c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+             q=torch.empty((M, N), dtype=torch.uint8, device="cuda"),
+             qs=torch.empty((M, N // 32), dtype=torch.uint8, device="cuda"),
+             g=dev_bf16(g_host),
+             gq=torch.empty((256, 1024), dtype=torch.uint8, device="cuda"),
+             gs=torch.empty((256, 32), dtype=torch.uint8, device="cuda"),
+             tq=torch.empty((1024, 256), dtype=torch.uint8, device="cuda"),
+             ts=torch.empty((1024, 8), dtype=torch.uint8, device="cuda"))
+    outs = ("c", "q", "qs", "gq", "gs", "tq", "ts")
+
+    def calls(stream=None):
+        mx.mx_gemm_fp8_fp4_splitk(d["a"], d["a_s"], d["b"], d["b_s"], d["c"], d["ws"],
+                                  bias=d["bias"], stream=stream)
+        mx.mx_gemm_fp8_fp4_quant(d["a"], d["a_s"], d["b"], d["b_s"], d["q"], d["qs"],
+                                 bias=d["bias"], stream=stream)
+        mx.mx_quant_e5m2(d["g"], d["gq"], d["gs"], seed=1234, stream=stream)
+        mx.mx_quant_transpose_e5m2(d["g"], d["tq"], d["ts"], seed=1234, stream=stream)
+
+    def snap():
+        torch.cuda.synchronize()
+        return {k: d[k].view(torch.uint8).cpu().numpy().copy() for k in outs}
+
+    note("graph 2: eager run")
+    calls()
+    eager = snap()
+    assert int(d["ws"][:65 * 4].count_nonzero()) == 0
+    # the stochastic codes against the oracle's Philox draws
+    oq, os_ = O.grad_quant_e5m2(g_host, seed=1234)
+    assert np.array_equal(eager["gq"], oq) and np.array_equal(eager["gs"], os_)
+    tq, ts = O.quant_transpose_e5m2(g_host, seed=1234)
+    assert np.array_equal(eager["tq"], tq) and np.array_equal(eager["ts"], ts)
+
+    note("graph 2: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for i in range(4):
+        for k in outs:
+            d[k].view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        note(f"graph 2: replay {i}")
+        g.replay()
+        got = snap()
+        for k in outs:
+            assert np.array_equal(got[k], eager[k]), (i, k)
+        assert int(d["ws"][:65 * 4].count_nonzero()) == 0, i
+    del g
