@@ -158,3 +158,46 @@ def test_skinny_fp4_shape_needs_no_workspace(mx):
     w, a, a_s, A, B = _operands("fp4_fp4", M, N, K, seed=4, with_bias=True)
     note("gemm splitk skinny shape, no workspace")
     _check_full(_run(mx, "fp4_fp4", a, a_s, w, None, M, N), A, B, w)
+
+
+def test_concurrent_streams_give_single_stream_bytes(mx):
+    # The library keeps no state between calls except a split call's workspace counters, so two
+    # split GEMMs with workspaces of their own and a quantizer, each on its own stream (default
+    # priority) and running at the same time, give the bytes of the same calls run one by one.
+    M, N, K = 1280, 3328, 5120
+    wsz = mx.mx_gemm_splitk_workspace_size(M, N, K)
+    ins = []
+    for seed in (31, 32):
+        w, a, a_s, A, B = _operands("fp8_fp4", M, N, K, seed=seed, with_bias=True)
+        ins.append((dev_u8(a), dev_u8(a_s), dev_u8(w.b), dev_u8(w.b_s), dev_bf16(w.bias),
+                    torch.zeros(wsz, dtype=torch.uint8, device="cuda"),
+                    torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    x = dev_bf16(synth.bf16_normal(synth.rng_for(33), (4096, 2048)))
+    q = torch.empty((4096, 2048), dtype=torch.uint8, device="cuda")
+    s = torch.empty((4096, 64), dtype=torch.uint8, device="cuda")
+
+    def run_all(streams):
+        for (a, a_s, b, b_s, bias, ws, c), st in zip(ins, streams[:2]):
+            mx.mx_gemm_fp8_fp4_splitk(a, a_s, b, b_s, c, ws, bias=bias, stream=st)
+        mx.mx_act_quant(x, q, s, stream=streams[2])
+
+    note("concurrent streams: one stream")
+    cur = torch.cuda.current_stream()
+    run_all([cur, cur, cur])
+    torch.cuda.synchronize()
+    ref = [host_bf16_bits(t[6]) for t in ins] + [q.cpu().numpy(), s.cpu().numpy()]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for rep in range(3):
+        for t in ins:
+            t[6].view(torch.int16).fill_(-1)
+        q.fill_(0xA5)
+        s.fill_(0xA5)
+        torch.cuda.synchronize()
+        note(f"concurrent streams: run {rep}")
+        run_all(streams)
+        torch.cuda.synchronize()
+        got = [host_bf16_bits(t[6]) for t in ins] + [q.cpu().numpy(), s.cpu().numpy()]
+        for i, (g, r) in enumerate(zip(got, ref)):
+            assert np.array_equal(g, r), (rep, i)
+        for t in ins:
+            assert int(t[5][:65 * 4].count_nonzero()) == 0
