@@ -530,13 +530,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
   bf16x8 fa[2][TM], fb[2][TN];
 
-  // The tile's bias as fp32 in LDS, written before the prologue's barrier and read by the
-  // epilogue: its load latency is hidden behind the main loop.
+  // The tile's bias as fp32 in LDS for the epilogue: thread c loads column c here, with the
+  // first step's operand loads behind it, and stores it to LDS just before the prologue's
+  // barrier, so its latency is hidden behind theirs.
+  static_assert(BN <= NT, "one bias value per thread");
   float* const lds_bias = reinterpret_cast<float*>(lds + lds_tile_bytes<AF, BF, BM, BN>());
-  if (BIAS && (EPI == kEpiPlain || p.bias != nullptr)) {
-    for (int c = threadIdx.x; c < BN; c += NT)
-      lds_bias[c] = bf16_bits_to_f32(p.bias[bz * p.stride_bias + min(n0 + c, p.N - 1)]);
-  }
+  const bool has_bias = BIAS && (EPI == kEpiPlain || p.bias != nullptr);
+  uint32_t bias_bits = 0;        // raw, so that nothing waits for the load before the store
+  if (has_bias)
+    bias_bits = p.bias[bz * p.stride_bias +
+                       min(n0 + min(static_cast<int>(threadIdx.x), BN - 1), p.N - 1)];
 
   // Pipeline: step k's codes are staged into LDS stage k & 1 during step k-1, piece by piece, and
   // each piece is reloaded for step k+1 right after it is staged.  Steps [k0, k0 + KT) of the
@@ -560,6 +563,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
       sb.template load_part<P>(k0 + 1, last_partial == k0 + 1);
     });
   }
+  if (has_bias && static_cast<int>(threadIdx.x) < BN)
+    lds_bias[threadIdx.x] = bf16_bits_to_f32(bias_bits);
   __syncthreads();
   br.take_scales();
   read_a<TM>(lds, a_base, coff[0], fa[0]);
@@ -662,24 +667,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     // outputs' places and overwrites them with the results.  The residual may be the output
     // itself: every read of the tile precedes the barrier before the copy-out.
     const uint16_t* res = p.res + bz * p.stride_res;
-    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-      const int row = m0 + trow, col = n0 + tch * 8;
-      const int ch = tile_ch(trow, tch);
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (row < p.M && col < p.N) {
-        const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
-        if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-          v = *reinterpret_cast<const uint4*>(src);
-        } else {
-          uint32_t e[8];
+    constexpr int kResStep = NT / kChunksPerRow;   // rows between a thread's chunks
+    constexpr int kResIters = BM / kResStep;
+    static_assert(NT % kChunksPerRow == 0 && BM % kResStep == 0, "residual rows");
+    if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
+        (reinterpret_cast<uintptr_t>(res) & 15u) == 0) {
+      // A tile inside a residual whose rows are 16-byte aligned: every thread loads its chunk
+      // column of all the tile's rows before storing any of it, so the loads are in flight
+      // together instead of one memory round trip per chunk.
+      const int trow0 = threadIdx.x / kChunksPerRow, tch = threadIdx.x % kChunksPerRow;
+      const uint16_t* src = res + static_cast<int64_t>(m0 + trow0) * p.N + n0 + tch * 8;
+      const int64_t step = static_cast<int64_t>(kResStep) * p.N;
+      uint4 v[kResIters];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) e[k] = col + k < p.N ? src[k] : 0u;
-          v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                    e[6] | (e[7] << 16)};
-        }
+      for (int it = 0; it < kResIters; ++it) v[it] = *reinterpret_cast<const uint4*>(src + it * step);
+#pragma unroll
+      for (int it = 0; it < kResIters; ++it) {
+        const int trow = trow0 + it * kResStep;
+        *reinterpret_cast<uint4*>(lds + trow * kTileRow + tile_ch(trow, tch) * 16) = v[it];
       }
-      *reinterpret_cast<uint4*>(lds + trow * kTileRow + ch * 16) = v;
+    } else {
+      for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+        const int row = m0 + trow, col = n0 + tch * 8;
+        const int ch = tile_ch(trow, tch);
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (row < p.M && col < p.N) {
+          const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
+          if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+            v = *reinterpret_cast<const uint4*>(src);
+          } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = col + k < p.N ? src[k] : 0u;
+            v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                      e[6] | (e[7] << 16)};
+          }
+        }
+        *reinterpret_cast<uint4*>(lds + trow * kTileRow + ch * 16) = v;
+      }
     }
     __syncthreads();
   }
@@ -689,7 +715,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     for (int r4 = 0; r4 < 4; ++r4) {
       const int tcol = wn * WTN + 32 * j + 8 * r4 + 4 * h;        // columns tcol .. tcol + 3
       v4f bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (BIAS && (EPI == kEpiPlain || p.bias != nullptr))
+      if (has_bias)
         bias4 = *reinterpret_cast<const v4f*>(lds_bias + tcol);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
