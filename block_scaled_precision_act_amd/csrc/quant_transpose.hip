@@ -34,14 +34,25 @@ __global__ __launch_bounds__(kQThreads) void quant_transpose_kernel(
     int C, uint64_t seed) {
   __shared__ uint4 tile[kTR * kTC / 8];
   const int r0 = blockIdx.y * kTR, c0 = blockIdx.x * kTC;
+  // All of a thread's loads are issued before any of them is stored to LDS (one memory round
+  // trip, not one per load); a tile wholly inside the matrix loads without bounds checks.
+  constexpr int kLoads = kTR * kTC / 8 / kQThreads;
+  const bool whole = r0 + kTR <= R && c0 + kTC <= C;
+  uint4 vin[kLoads];
 #pragma unroll
-  for (int i = 0; i < kTR * kTC / 8 / kQThreads; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int idx = static_cast<int>(threadIdx.x) + i * kQThreads;
     const int r = idx >> 3, j = idx & 7;
     const int gr = r0 + r, gc = c0 + j * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (gr < R && gc < C) v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(gr) * C + gc);
-    tile[r * 8 + (j ^ (2 * ((r >> 5) & 3)))] = v;
+    vin[i] = make_uint4(0, 0, 0, 0);
+    if (whole || (gr < R && gc < C))
+      vin[i] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(gr) * C + gc);
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int idx = static_cast<int>(threadIdx.x) + i * kQThreads;
+    const int r = idx >> 3, j = idx & 7;
+    tile[r * 8 + (j ^ (2 * ((r >> 5) & 3)))] = vin[i];
   }
   __syncthreads();
 
