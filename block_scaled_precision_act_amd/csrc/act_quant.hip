@@ -12,8 +12,10 @@
 // matrix is one flat run of 32-blocks and scale byte i belongs to elements [32i, 32i+32).
 // Each lane owns 16-byte chunks (8 bf16); the four lanes of a DPP quad own one block, so the
 // block max needs two quad permutes and no LDS.  Loads are 16 B, stores of codes are 8 B per lane
-// (512 contiguous bytes per wavefront), the scale byte is written by the quad's first lane; code
-// and scale stores are non-temporal (streamed past the caches).
+// (512 contiguous bytes per wavefront), the scale byte is written by the quad's first lane.  Every
+// input is read once and every output written once, so loads and stores are all non-temporal
+// (streamed past the caches): on a [16384, 7168] input the non-temporal loads measured 55 us
+// against 59 us for cached ones.
 #include "mx_internal.h"
 #include "mx_philox.h"
 #include "mx_quant.h"
@@ -23,11 +25,23 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+__device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
+  __builtin_nontemporal_store(v2u32{v.x, v.y}, reinterpret_cast<v2u32*>(p));
+}
+
 // grid.x covers ceil(chunks / (kThreads * UNROLL)) slots, grid.y is the batch index.
-// UNROLL: 16-byte chunks in flight per lane; NT: non-temporal code and scale stores.
+// UNROLL: 16-byte chunks in flight per lane.
 // STOCH (E5M2 only): chunk c of batch b holds output elements 8 (b * chunks + c) + j, j < 8, whose
 // uniforms are the eight 32-bit words of Philox block b * chunks + c under the seed.
-template <int UNROLL, bool NT, int FMT, bool STOCH = false>
+template <int UNROLL, int FMT, bool STOCH = false>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
     int64_t chunks, int64_t stride_x, int64_t stride_q, int64_t stride_s, uint64_t seed) {
@@ -41,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
     const int64_t c = base + u * kThreads;
-    w[u] = c < chunks ? xv[c] : make_uint4(0, 0, 0, 0);
+    w[u] = c < chunks ? load_stream(xv + c) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
@@ -63,8 +77,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
         codes.y = encode4_e5m2(w[u].z, w[u].w, inv_s);
       }
       if (c < chunks) {
-        __builtin_nontemporal_store(codes.x, reinterpret_cast<uint32_t*>(qv + c));
-        __builtin_nontemporal_store(codes.y, reinterpret_cast<uint32_t*>(qv + c) + 1);
+        store_stream(qv + c, codes);
         if ((threadIdx.x & 3) == 0) __builtin_nontemporal_store(static_cast<uint8_t>(byte), sv + (c >> 2));
       }
       continue;
@@ -80,19 +93,13 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     }
     const QuantChunk qc = quant_chunk(w[u]);
     if (c < chunks) {
-      if (NT) {
-        __builtin_nontemporal_store(qc.codes.x, reinterpret_cast<uint32_t*>(qv + c));
-        __builtin_nontemporal_store(qc.codes.y, reinterpret_cast<uint32_t*>(qv + c) + 1);
-        if ((threadIdx.x & 3) == 0) __builtin_nontemporal_store(static_cast<uint8_t>(qc.byte), sv + (c >> 2));
-      } else {
-        qv[c] = qc.codes;
-        if ((threadIdx.x & 3) == 0) sv[c >> 2] = static_cast<uint8_t>(qc.byte);
-      }
+      store_stream(qv + c, qc.codes);
+      if ((threadIdx.x & 3) == 0) __builtin_nontemporal_store(static_cast<uint8_t>(qc.byte), sv + (c >> 2));
     }
   }
 }
 
-template <int UNROLL, bool NT, int FMT, bool STOCH = false>
+template <int UNROLL, int FMT, bool STOCH = false>
 hipError_t launch_act_quant_v(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
                               int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
                               hipStream_t stream, uint64_t seed = 0) {
@@ -100,7 +107,7 @@ hipError_t launch_act_quant_v(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t
   const int64_t per_block = static_cast<int64_t>(kThreads) * UNROLL;
   const int64_t blocks = (chunks + per_block - 1) / per_block;
   dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(batch));
-  hipLaunchKernelGGL((act_quant_kernel<UNROLL, NT, FMT, STOCH>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((act_quant_kernel<UNROLL, FMT, STOCH>), grid, dim3(kThreads), 0, stream,
                      x, q, s, chunks, stride_x, stride_q, stride_s, seed);
   return hipGetLastError();
 }
@@ -110,16 +117,16 @@ hipError_t launch_act_quant_v(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t
 hipError_t launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* s, int64_t M, int64_t K,
                             int64_t batch, int64_t stride_x, int64_t stride_q, int64_t stride_s,
                             hipStream_t stream, int fmt, bool stochastic, uint64_t seed) {
-  // Two 16-byte chunks per lane and non-temporal stores measured best for sustained streaming
-  // (inputs and outputs far larger than the last-level cache).
+  // Two 16-byte chunks per lane measured best for sustained streaming (inputs and outputs far
+  // larger than the last-level cache).
   if (fmt == kBf8 && stochastic)
-    return launch_act_quant_v<2, true, kBf8, true>(x, q, s, M, K, batch, stride_x, stride_q,
+    return launch_act_quant_v<2, kBf8, true>(x, q, s, M, K, batch, stride_x, stride_q,
                                                    stride_s, stream, seed);
   if (fmt == kBf8)
-    return launch_act_quant_v<2, true, kBf8>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
+    return launch_act_quant_v<2, kBf8>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
   if (fmt == kFp4)
-    return launch_act_quant_v<2, true, kFp4>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
-  return launch_act_quant_v<2, true, kFp8>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
+    return launch_act_quant_v<2, kFp4>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
+  return launch_act_quant_v<2, kFp8>(x, q, s, M, K, batch, stride_x, stride_q, stride_s, stream);
 }
 
 }  // namespace mx
