@@ -45,6 +45,9 @@ GEMM_SOURCES = ["block_scaled_precision_act_amd/csrc/gemm_bf16.hip",
 ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip",
                      "block_scaled_precision_act_amd/csrc/mx_philox.h",
                      "block_scaled_precision_act_amd/csrc/mx_quant.h"]
+# act_quant_kernel<chunks per lane, output format, stochastic>: format 0 is E4M3, 4 packed E2M1
+AQ_E4M3_KERNEL = r"act_quant_kernel<\d+, 0, false>"
+AQ_E2M1_KERNEL = r"act_quant_kernel<\d+, 4, false>"
 COPY_BYTES = 1 << 30          # the plain copy used to calibrate the HBM byte counters
 COPY_REPS = 3                 # ... run this many times, last in the program
 
@@ -583,13 +586,12 @@ def _timed_region_averages(stats_dir):
     g = gall[warmup:warmup + steps]
     if g:
         res["gemm_fp8_fp4 (inside the timed steps)"] = (len(g), sum(g) / len(g), None)
-    big = max((gr for _, k, _, gr in seq if re.search(r"act_quant_kernel<\d+, \w+, 0, false>", k)),
-              default=None)
-    a8 = durs(r"act_quant_kernel<\d+, \w+, 0, false>", big)[6:]
+    big = max((gr for _, k, _, gr in seq if re.search(AQ_E4M3_KERNEL, k)), default=None)
+    a8 = durs(AQ_E4M3_KERNEL, big)[6:]
     ev = line.get("act_quant", {}).get("avg_launch_ms")
     if a8:
         res["act_quant [16384, 7168]"] = (len(a8), sum(a8) / len(a8), ev and ev * 1e3)
-    a4 = durs(r"act_quant_kernel<\d+, \w+, 4, false>")[6:]
+    a4 = durs(AQ_E2M1_KERNEL)[6:]
     ev = line.get("act_quant_fp4", {}).get("avg_launch_ms")
     if a4:
         res["act_quant_fp4 [16384, 7168]"] = (len(a4), sum(a4) / len(a4), ev and ev * 1e3)
@@ -647,10 +649,8 @@ def summarize(stats_dir, fetch_dir, write_dir):
     copy_f, copy_w = calib(fetch), calib(write)
     f_factor = copy_f / COPY_BYTES if copy_f else None
     w_factor = copy_w / COPY_BYTES if copy_w else None
-    # act_quant on [16384, 7168]: the act_quant dispatches with the largest grid; the third
-    # template argument of the kernel is the output format (0: E4M3, 4: E2M1, 1: E5M2), the
-    # fourth the stochastic rounding of E5M2
-    aq8, aq4 = r"act_quant_kernel<\d+, \w+, 0, false>", r"act_quant_kernel<\d+, \w+, 4, false>"
+    # act_quant on [16384, 7168]: the E4M3 act_quant dispatches with the largest grid
+    aq8, aq4 = AQ_E4M3_KERNEL, AQ_E2M1_KERNEL
     aq_grids = [g for (k, g, _) in list(fetch) + list(write) if re.search(aq8, k)]
     aq_grid = max(aq_grids) if aq_grids else None
     aq_alg = ACT_QUANT_BYTES_PER_ELEM * 16384 * 7168
