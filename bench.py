@@ -48,6 +48,14 @@ ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip",
 # act_quant_kernel<chunks per lane, output format, stochastic>: format 0 is E4M3, 4 packed E2M1
 AQ_E4M3_KERNEL = r"act_quant_kernel<\d+, 0, false>"
 AQ_E2M1_KERNEL = r"act_quant_kernel<\d+, 4, false>"
+# gemm_bf16_kernel<A format, B format, bias, quantized output, epilogue, split-K, BM, BN, ...>:
+# format 0 is E4M3, 4 packed E2M1
+GEMM_FP8_FP4_KERNEL = r"gemm_bf16_kernel<0, 4, true, false, 0, false, 256, 256,"
+GEMM_FP8_FP4_QUANT_KERNEL = r"gemm_bf16_kernel<0, 4, true, true, 0, false, 256, 256,"
+GEMM_FP8_FP4_128_KERNEL = r"gemm_bf16_kernel<0, 4, true, false, 0, false, 128, 128,"
+GEMM_FP8_FP4_SPLITK_KERNEL = r"gemm_bf16_kernel<0, 4, true, false, 0, true, 256, 256,"
+KERNEL_PATTERNS = (AQ_E4M3_KERNEL, AQ_E2M1_KERNEL, GEMM_FP8_FP4_KERNEL, GEMM_FP8_FP4_QUANT_KERNEL,
+                   GEMM_FP8_FP4_128_KERNEL, GEMM_FP8_FP4_SPLITK_KERNEL)
 COPY_BYTES = 1 << 30          # the plain copy used to calibrate the HBM byte counters
 COPY_REPS = 3                 # ... run this many times, last in the program
 
@@ -578,7 +586,7 @@ def _timed_region_averages(stats_dir):
 
     res = {}
     # the GEMM's dispatches: warm-up steps, timed steps, then the back-to-back GEMM loop
-    gall = durs(r"gemm_bf16_kernel<0, 4, true, false, 0, false, 256, 256,")
+    gall = durs(GEMM_FP8_FP4_KERNEL)
     g = gall[warmup + steps:warmup + 2 * steps]
     ev = line.get("roofline", {}).get("avg_launch_ms")
     if g:
@@ -595,7 +603,7 @@ def _timed_region_averages(stats_dir):
     ev = line.get("act_quant_fp4", {}).get("avg_launch_ms")
     if a4:
         res["act_quant_fp4 [16384, 7168]"] = (len(a4), sum(a4) / len(a4), ev and ev * 1e3)
-    q = durs(r"gemm_bf16_kernel<0, 4, true, true, 0, false, 256, 256,")[5:]
+    q = durs(GEMM_FP8_FP4_QUANT_KERNEL)[5:]
     ev = line.get("next_layer_quant", {}).get("fused_ms")
     if q:
         res["gemm_fp8_fp4_quant (fused next layer)"] = (len(q), sum(q) / len(q), ev and ev * 1e3)
@@ -661,17 +669,16 @@ def summarize(stats_dir, fetch_dir, write_dir):
     # the split-K line's down-projection 4096x2048x7168 (its partial tiles are not algorithmic)
     down_alg = 4096 * 7168 + 4096 * 224 + 2048 * 3584 + 2048 * 224 + 2 * 2048 + 2 * 4096 * 2048
     out = {}
-    # template arguments <A format, B format, bias, quantized output, ...> pick the variant
     for name, part, grid, files, alg in (
             ("act_quant_16384x7168", aq8, aq_grid, ACT_QUANT_SOURCES, aq_alg),
             ("act_quant_fp4_16384x7168", aq4, None, ACT_QUANT_SOURCES, aq4_alg),
-            ("gemm_fp8_fp4_4096x7168x2048", r"gemm_bf16_kernel<0, 4, true, false, 0, false, 256, 256,", None,
+            ("gemm_fp8_fp4_4096x7168x2048", GEMM_FP8_FP4_KERNEL, None,
              GEMM_SOURCES, gemm_alg),
-            ("gemm_fp8_fp4_quant_4096x7168x2048", r"gemm_bf16_kernel<0, 4, true, true, 0, false, 256, 256,", None,
+            ("gemm_fp8_fp4_quant_4096x7168x2048", GEMM_FP8_FP4_QUANT_KERNEL, None,
              GEMM_SOURCES, gemm_q_alg),
-            ("gemm_fp8_fp4_4096x2048x7168_plain", r"gemm_bf16_kernel<0, 4, true, false, 0, false, 128, 128,",
+            ("gemm_fp8_fp4_4096x2048x7168_plain", GEMM_FP8_FP4_128_KERNEL,
              None, GEMM_SOURCES, down_alg),
-            ("gemm_fp8_fp4_4096x2048x7168_splitk", r"gemm_bf16_kernel<0, 4, true, false, 0, true, 256, 256,",
+            ("gemm_fp8_fp4_4096x2048x7168_splitk", GEMM_FP8_FP4_SPLITK_KERNEL,
              None, GEMM_SOURCES, down_alg)):
         f, w = pick(fetch, part, grid), pick(write, part, grid)
         if f is None or w is None or not f_factor or not w_factor:
