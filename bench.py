@@ -7,6 +7,7 @@ E8M0 scales, then the FP8 x MXFP4 GEMM against E2M1 weights [7168, 2048] (per-32
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
     python bench.py --summarize STATS_DIR FETCH_DIR WRITE_DIR   (CPU only; writes profiles/)
+    python bench.py --summarize-busy BUSY_DIR                   (CPU only; writes profiles/)
 
 Prints one JSON line.  `value` is the GEMM's 2*M*N*K flops divided by the time of a whole step
 (act_quant included), in TFLOP/s.  `roofline` is the dominant kernel (the GEMM): as many
@@ -81,6 +82,20 @@ def _traffic(kernel: str, files):
     return d.get("hbm_bytes_per_launch")
 
 
+def _mfma_util(kernel: str, files):
+    """MFMA utilisation of `kernel` (rocprofv3's MfmaUtil: MFMA-busy cycles over the SIMD cycles
+    of the active GPU) from the committed counter summary, when it was taken on the current
+    source (else None)."""
+    p = os.path.join(HERE, "profiles", f"mfma_util_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != _kernel_hash(files):
+        return None
+    return d.get("mfma_util")
+
+
 def time_events(fn, iters, torch):
     """Average time per fn() over iters back-to-back calls: one pair of HIP events on the current
     stream (the stream every launch here goes to) brackets the whole run, so the figure is the
@@ -138,9 +153,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-busy", metavar="BUSY_DIR")
     args = ap.parse_args()
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.summarize_busy:
+        summarize_busy(args.summarize_busy)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this hot path has no "
@@ -203,6 +222,7 @@ def main():
                 "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / MFMA_PEAK_TFLOPS["bf16"], 4),
                 "traffic": _traffic("gemm_fp8_fp4_4096x7168x2048", GEMM_SOURCES),
+                "mfma_util": _mfma_util("gemm_fp8_fp4_4096x7168x2048", GEMM_SOURCES),
                 "kernel": "gemm_bf16_kernel<fp8, fp4, bias> (E4M3/E2M1 decoded exactly to bf16, "
                           "bf16 MFMA)", "avg_launch_ms": round(gemm_ms, 5),
                 "algorithmic_flops_per_launch": flops,
@@ -735,6 +755,79 @@ def summarize(stats_dir, fetch_dir, write_dir):
     with open(os.path.join(prof, "traffic_act_quant_16384x7168_and_gemm_fp8_fp4_4096x7168x2048.txt"), "w") as fh:
         fh.write("\n".join(tl) + "\n")
     print("\n".join(lines + [""] + tl))
+
+
+BUSY_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE "
+                 "SQ_INSTS_MFMA")
+
+
+def summarize_busy(busy_dir):
+    """MFMA utilisation of the 4096x7168x2048 GEMM from one rocprofv3 --pmc run of BUSY_COUNTERS
+    with --kernel-trace (the trace gives each dispatch's duration).  Counter values in the csv are
+    sums over the XCDs and shader engines.  Per dispatch:
+    * active cycles g = GRBM_GUI_ACTIVE / XCDs (the GUI counter runs once per XCD), clock = g / ns;
+    * mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (g * SIMDs), rocprofv3's own MfmaUtil;
+    * cu_busy = SQ_BUSY_CU_CYCLES / (g * CUs), and mfma_busy_over_busy_cu = MFMA-busy cycles over
+      the SIMD cycles of CUs that hold a workgroup.  SQ_BUSY_CU_CYCLES is read in plain cycles:
+      read as quad-cycles it would exceed CUs * g threefold.
+    Medians over the dispatches are written to profiles/mfma_util_<kernel>.json and .txt."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(pattern):
+        files = glob.glob(os.path.join(busy_dir, "**", pattern), recursive=True)
+        return [r for f in files for r in csv.DictReader(open(f))]
+
+    agent = [r for r in rows("*agent_info.csv") if r.get("Name", "").startswith("gfx")][0]
+    simds, cus, xcds = int(agent["Simd_Count"]), int(agent["Cu_Count"]), int(agent["Num_Xcc"])
+    dur = {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+           for r in rows("*kernel_trace.csv")}
+    ctr = {}
+    for r in rows("*counter_collection.csv"):
+        if re.search(GEMM_FP8_FP4_KERNEL, r["Kernel_Name"]):
+            ctr.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    per = []
+    for did, v in ctr.items():
+        if did not in dur or len(v) < len(BUSY_COUNTERS.split()):
+            continue
+        g = v["GRBM_GUI_ACTIVE"] / xcds
+        per.append({"duration_us": dur[did] / 1000.0, "clock_ghz": g / dur[did],
+                    "mfma_util": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds),
+                    "cu_busy": v["SQ_BUSY_CU_CYCLES"] / (g * cus),
+                    "mfma_busy_over_busy_cu": v["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                              (v["SQ_BUSY_CU_CYCLES"] * simds / cus),
+                    "mfma_insts": v["SQ_INSTS_MFMA"],
+                    "mfma_busy_cycles_per_inst": v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["SQ_INSTS_MFMA"]})
+    if not per:
+        print("no GEMM dispatches with every counter found", file=sys.stderr)
+        return
+    med = {k: round(statistics.median(d[k] for d in per), 4) for k in per[0]}
+    M, N, K = 4096, 7168, 2048
+    cmd = (f"rocprofv3 --pmc {BUSY_COUNTERS} --kernel-trace --output-format csv -d OUT/busy -o run "
+           "-- python3 bench.py --steps 2 --warmup 1 --no-cpu --aq-iters 2")
+    out = {"source_hash": _kernel_hash(GEMM_SOURCES), "dispatches": len(per),
+           "simds": simds, "cus": cus, "xcds": xcds,
+           "mfma_insts_expected": 2 * M * N * K // (32 * 32 * 16 * 2), **med, "command": cmd}
+    prof = os.path.join(HERE, "profiles")
+    name = "mfma_util_gemm_fp8_fp4_4096x7168x2048"
+    with open(os.path.join(prof, name + ".json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    txt = [f"MFMA utilisation of the FP8xMXFP4 GEMM 4096x7168x2048 + bias (bf16 MFMA 32x32x16),",
+           f"medians over {len(per)} dispatches of one counter run:", "",
+           "command (TMPDIR=/tmp, repository root as cwd, OUT the folder the profiler writes to):",
+           "  " + cmd, "  python bench.py --summarize-busy OUT/busy", "",
+           f"duration {med['duration_us']} us at {med['clock_ghz']} GHz "
+           f"(GRBM_GUI_ACTIVE over the {xcds} XCDs / duration)",
+           f"MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x {simds} SIMDs) = {med['mfma_util']}",
+           f"CUs holding a workgroup: {med['cu_busy']} of the active cycles; MFMA-busy over their "
+           f"SIMD cycles = {med['mfma_busy_over_busy_cu']}",
+           f"MFMA instructions {med['mfma_insts']:.0f} (2MNK/32768 = {out['mfma_insts_expected']}), "
+           f"{med['mfma_busy_cycles_per_inst']} busy cycles each",
+           f"source hash {out['source_hash']}"]
+    with open(os.path.join(prof, name + ".txt"), "w") as fh:
+        fh.write("\n".join(txt) + "\n")
+    print("\n".join(txt))
 
 
 if __name__ == "__main__":
