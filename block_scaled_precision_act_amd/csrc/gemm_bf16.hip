@@ -398,17 +398,20 @@ __device__ __forceinline__ void read_a(const uint8_t* stage, uint32_t a_base, ui
 // The other work of a sub-step is cut into tasks (an A fragment read, a raw B read, a B tile
 // decode, one staged chunk) that are spread evenly over the slots after its MFMAs; each slot is
 // fenced from the scheduler so the matrix pipe gets an MFMA between every few other instructions.
-template <bool MORE, bool RELOAD, int TM, int TN, class SA, class SB, class BR>
+template <bool MORE, bool RELOAD, int FA, int TM, int TN, class SA, class SB, class BR>
 __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_t a_base,
                                        const uint32_t (&coff)[4], SA& sa, SB& sb, BR& br,
-                                       bf16x8 (&fa)[2][TM], bf16x8 (&fb)[2][TN],
+                                       bf16x8 (&fa)[FA][TM], bf16x8 (&fb)[2][TN],
                                        v16f (&acc)[TM][TN], int kt_load, bool partial_load) {
   static_for<0, 4>([&](auto sc) {
     constexpr int s = decltype(sc)::value;
     constexpr int nb = (s + 1) & 1;                                      // operand buffer filled
     constexpr bool last = s == 3;
     constexpr int kRaw = (last && MORE) ? TN * BR::kQ : 0;               // raw B reads of nxt
-    constexpr int kRd = (!last || MORE) ? TM : 0;                         // A fragment reads
+    // A fragment reads: one sub-step ahead, or (FA == 4) all four sub-steps of the next K step
+    // after the barrier, so a wavefront with one MFMA per sub-step waits for LDS once per step.
+    constexpr bool kAllRead = FA == 4;
+    constexpr int kRd = kAllRead ? ((last && MORE) ? 4 * TM : 0) : ((!last || MORE) ? TM : 0);
     constexpr int kDec = (!last || MORE) ? TN : 0;                        // B tile decodes
     constexpr int kA = (!last && MORE) ? SA::template chunks_in_part<s>() : 0;
     constexpr int kB = (!last && MORE) ? SB::template chunks_in_part<s>() : 0;
@@ -423,6 +426,9 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
       constexpr int t = decltype(tc)::value;
       if constexpr (t < kRaw) {
         br.template read_raw<t / BR::kQ, t % BR::kQ>(nxt);
+      } else if constexpr (t < kRaw + kRd && kAllRead) {
+        constexpr int sub = (t - kRaw) / TM, i = (t - kRaw) % TM;
+        fa[sub][i] = *reinterpret_cast<const bf16x8*>(nxt + a_base + i * 32 * kRowBytes + coff[sub]);
       } else if constexpr (t < kRaw + kRd) {
         constexpr int i = t - kRaw;
         const uint8_t* stage = last ? nxt : cur;
@@ -440,8 +446,8 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
     static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       constexpr int i = m / TN, j = m % TN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i], acc[i][j],
-                                                          0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[kAllRead ? s : s & 1][i],
+                                                          acc[i][j], 0, 0, 0);
       static_for<m * kTasks / kM, (m + 1) * kTasks / kM>(task);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -528,7 +534,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
-  bf16x8 fa[2][TM], fb[2][TN];
+  // One 32x32 block per wavefront: its four sub-steps' A fragments are read together.
+  constexpr int kFa = TM * TN == 1 ? 4 : 2;
+  bf16x8 fa[kFa][TM], fb[2][TN];
 
   // The tile's bias as fp32 in LDS for the epilogue: thread c loads column c here, with the
   // first step's operand loads behind it, and stores it to LDS just before the prologue's
@@ -567,7 +575,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
     lds_bias[threadIdx.x] = bf16_bits_to_f32(bias_bits);
   __syncthreads();
   br.take_scales();
-  read_a<TM>(lds, a_base, coff[0], fa[0]);
+  static_for<0, kFa == 4 ? 4 : 1>([&](auto kc) {
+    constexpr int ks = decltype(kc)::value;
+    read_a<TM>(lds, a_base, coff[ks], fa[ks]);
+  });
   br.read_raw_all(lds);
   br.template decode_all<0>(fb[0]);
   if (KT > 1) br.load_scales(k0 + 1);
