@@ -36,6 +36,8 @@
 //     for 16-byte row stores; or, for the quantizing entry points, the same bf16 tile quantized
 //     per 32 columns to E4M3 + E8M0 (the next layer's activation operand) without writing the
 //     bf16 values out.
+#include <atomic>
+
 #include "mx_epilogue.h"
 #include "mx_internal.h"
 #include "mx_quant.h"
@@ -826,20 +828,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
 
 template <int AF, int BF, bool BIAS, bool QUANT, int EPI, int BM, int BN, int WM, int WN,
           bool SPLIT = false>
-hipError_t launch_kernel(const Args& p, dim3 grid, hipStream_t stream) {
+hipError_t launch_kernel(const Args& p, dim3 grid, int device, hipStream_t stream) {
   constexpr int kLds = lds_bytes<AF, BF, BM, BN>();
   static_assert(kLds + 16 <= 160 * 1024, "LDS");
   auto k = gemm_bf16_kernel<AF, BF, BIAS, QUANT, EPI, SPLIT, BM, BN, WM, WN>;
-  // The dynamic-LDS limit is raised once per kernel (above 64 KB needs the attribute).
-  static const hipError_t attr_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-  if (attr_ok != hipSuccess) return attr_ok;
+  // The dynamic-LDS limit (above 64 KB needs the attribute) is raised once per kernel and device
+  // (device ids are below 64); two threads that race here both set the same value.
+  static std::atomic<uint64_t> raised{0};
+  const uint64_t bit = uint64_t{1} << (device & 63);
+  if ((raised.load(std::memory_order_acquire) & bit) == 0) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    raised.fetch_or(bit, std::memory_order_acq_rel);
+  }
   hipLaunchKernelGGL(k, grid, dim3(64 * WM * WN), kLds, stream, p);
   return hipGetLastError();
 }
 
 template <int AF, int BF, int BM, int BN, int WM, int WN>
-hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
+hipError_t launch_tile(const GemmProblem& g, int device, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          (g.M + BM - 1) / BM, (g.N + BN - 1) / BN,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
@@ -849,24 +857,25 @@ hipError_t launch_tile(const GemmProblem& g, hipStream_t stream) {
   if constexpr (AF == kFp8 || AF == kFp4) {
     if (g.q) {
       if (g.epi == kEpiGelu)
-        return launch_kernel<AF, BF, true, true, kEpiGelu, BM, BN, WM, WN>(p, grid, stream);
-      return g.bias ? launch_kernel<AF, BF, true, true, kEpiPlain, BM, BN, WM, WN>(p, grid, stream)
-                    : launch_kernel<AF, BF, false, true, kEpiPlain, BM, BN, WM, WN>(p, grid, stream);
+        return launch_kernel<AF, BF, true, true, kEpiGelu, BM, BN, WM, WN>(p, grid, device, stream);
+      return g.bias ? launch_kernel<AF, BF, true, true, kEpiPlain, BM, BN, WM, WN>(p, grid, device, stream)
+                    : launch_kernel<AF, BF, false, true, kEpiPlain, BM, BN, WM, WN>(p, grid, device, stream);
     }
   }
   if (g.epi == kEpiResidual)
-    return launch_kernel<AF, BF, true, false, kEpiResidual, BM, BN, WM, WN>(p, grid, stream);
+    return launch_kernel<AF, BF, true, false, kEpiResidual, BM, BN, WM, WN>(p, grid, device, stream);
   if (g.epi == kEpiGelu)
-    return launch_kernel<AF, BF, true, false, kEpiGelu, BM, BN, WM, WN>(p, grid, stream);
-  return g.bias ? launch_kernel<AF, BF, true, false, kEpiPlain, BM, BN, WM, WN>(p, grid, stream)
-                : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN>(p, grid, stream);
+    return launch_kernel<AF, BF, true, false, kEpiGelu, BM, BN, WM, WN>(p, grid, device, stream);
+  return g.bias ? launch_kernel<AF, BF, true, false, kEpiPlain, BM, BN, WM, WN>(p, grid, device, stream)
+                : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN>(p, grid, device, stream);
 }
 
 // Split-K launch: 256x256 tiles, grid = tiles * splits (one batch), bf16 output with an optional
 // bias.  The workspace holds the tile counters (zero on entry, left zero on exit) and then the
 // fp32 partial tiles.
 template <int AF, int BF>
-hipError_t launch_split(const GemmProblem& g, const SplitPlan& plan, hipStream_t stream) {
+hipError_t launch_split(const GemmProblem& g, const SplitPlan& plan, int device,
+                         hipStream_t stream) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
   uint8_t* ws = static_cast<uint8_t*>(g.workspace);
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
@@ -876,15 +885,15 @@ hipError_t launch_split(const GemmProblem& g, const SplitPlan& plan, hipStream_t
          reinterpret_cast<float*>(ws + plan.counter_bytes), reinterpret_cast<uint32_t*>(ws),
          plan.splits};
   dim3 grid(p.tiles_m * p.tiles_n * plan.splits, 1);
-  return g.bias ? launch_kernel<AF, BF, true, false, kEpiPlain, BM, BN, WM, WN, true>(p, grid, stream)
-                : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN, true>(p, grid, stream);
+  return g.bias ? launch_kernel<AF, BF, true, false, kEpiPlain, BM, BN, WM, WN, true>(p, grid, device, stream)
+                : launch_kernel<AF, BF, false, false, kEpiPlain, BM, BN, WM, WN, true>(p, grid, device, stream);
 }
 
 template <int AF, int BF>
 hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream_t stream) {
   if (g.workspace) {
     const SplitPlan plan = plan_split(g.M, g.N, g.K, g.batch);
-    if (plan.splits > 1) return launch_split<AF, BF>(g, plan, stream);
+    if (plan.splits > 1) return launch_split<AF, BF>(g, plan, dev.device, stream);
   }
   // Largest tile that still gives every CU a workgroup; the smallest one otherwise.
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
@@ -896,9 +905,9 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   // finishing them as 256 tiles of 256x192 in a second launch measured the same total time.
   // Above half the CUs, one wave of 256x256 tiles beats the three or four waves of 128x128 tiles
   // the same output needs (a 128x128 step costs 0.37 of a 256x256 step for a quarter of the work).
-  if (2 * tiles(256, 256) > cus) return launch_tile<AF, BF, 256, 256, 2, 4>(g, stream);
-  if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, stream);
-  return launch_tile<AF, BF, 64, 64, 2, 2>(g, stream);
+  if (2 * tiles(256, 256) > cus) return launch_tile<AF, BF, 256, 256, 2, 4>(g, dev.device, stream);
+  if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, dev.device, stream);
+  return launch_tile<AF, BF, 64, 64, 2, 2>(g, dev.device, stream);
 }
 
 }  // namespace

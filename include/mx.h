@@ -31,7 +31,8 @@
  *     MX_ERR_LAUNCH; faults inside a kernel surface at the caller's next synchronization.
  *   - Inputs the formats refuse are outside the contract and are NOT checked on the device:
  *     NaN E4M3 codes, scale byte 255, non-finite activations.  Their outputs are unspecified.
- *   - All entry points are thread-safe and stateless apart from a per-device capability cache.
+ *   - All entry points are thread-safe and stateless apart from a per-device capability cache and,
+ *     per kernel and device, the one-time raise of its dynamic LDS limit on first launch.
  */
 #ifndef MX_H_
 #define MX_H_
