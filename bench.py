@@ -761,7 +761,7 @@ BUSY_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM
                  "SQ_INSTS_MFMA")
 
 
-def summarize_busy(busy_dir):
+def summarize_busy(busy_dir, prof_dir=None):
     """MFMA utilisation of the 4096x7168x2048 GEMM from one rocprofv3 --pmc run of BUSY_COUNTERS
     with --kernel-trace (the trace gives each dispatch's duration).  Counter values in the csv are
     sums over the XCDs and shader engines.  Per dispatch:
@@ -770,7 +770,8 @@ def summarize_busy(busy_dir):
     * cu_busy = SQ_BUSY_CU_CYCLES / (g * CUs), and mfma_busy_over_busy_cu = MFMA-busy cycles over
       the SIMD cycles of CUs that hold a workgroup.  SQ_BUSY_CU_CYCLES is read in plain cycles:
       read as quad-cycles it would exceed CUs * g threefold.
-    Medians over the dispatches are written to profiles/mfma_util_<kernel>.json and .txt."""
+    Medians over the dispatches are written to mfma_util_<kernel>.json and .txt in prof_dir
+    (profiles/ by default) and returned."""
     import csv
     import glob
     import statistics
@@ -801,7 +802,7 @@ def summarize_busy(busy_dir):
                     "mfma_busy_cycles_per_inst": v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["SQ_INSTS_MFMA"]})
     if not per:
         print("no GEMM dispatches with every counter found", file=sys.stderr)
-        return
+        return None
     med = {k: round(statistics.median(d[k] for d in per), 4) for k in per[0]}
     M, N, K = 4096, 7168, 2048
     cmd = (f"rocprofv3 --pmc {BUSY_COUNTERS} --kernel-trace --output-format csv -d OUT/busy -o run "
@@ -809,7 +810,7 @@ def summarize_busy(busy_dir):
     out = {"source_hash": _kernel_hash(GEMM_SOURCES), "dispatches": len(per),
            "simds": simds, "cus": cus, "xcds": xcds,
            "mfma_insts_expected": 2 * M * N * K // (32 * 32 * 16 * 2), **med, "command": cmd}
-    prof = os.path.join(HERE, "profiles")
+    prof = prof_dir or os.path.join(HERE, "profiles")
     name = "mfma_util_gemm_fp8_fp4_4096x7168x2048"
     with open(os.path.join(prof, name + ".json"), "w") as fh:
         json.dump(out, fh, indent=1)
@@ -828,6 +829,7 @@ def summarize_busy(busy_dir):
     with open(os.path.join(prof, name + ".txt"), "w") as fh:
         fh.write("\n".join(txt) + "\n")
     print("\n".join(txt))
+    return out
 
 
 if __name__ == "__main__":

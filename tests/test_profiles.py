@@ -3,7 +3,8 @@
 bench.py finds the timed kernels in a kernel trace and in the counter runs by regular
 expressions over their demangled names (template arguments included), so a change to a kernel's
 template parameters must come with a change to those patterns, or the summaries silently lose
-those kernels.  This checks every pattern against the names in the committed trace summary.
+those kernels.  This checks every pattern against the names in the committed trace summary, and
+the MFMA-utilisation summary's arithmetic on a synthetic counter run.
 """
 import glob
 import json
@@ -41,3 +42,41 @@ def test_traffic_summaries_are_complete():
                     "traffic_over_algorithmic"):
             assert key in d, f"{os.path.basename(path)} lacks {key}"
         assert d["hbm_bytes_per_launch"] >= d["algorithmic_bytes_per_launch"] * 0.99, path
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w") as fh:
+        fh.write(",".join(header) + "\n")
+        for r in rows:
+            fh.write(",".join(f'"{v}"' if isinstance(v, str) else str(v) for v in r) + "\n")
+
+
+def test_summarize_busy_arithmetic(tmp_path):
+    """A synthetic counter run: 2 dispatches of the GEMM and one other kernel, counters summed over
+    8 XCDs as rocprofv3 writes them.  Active cycles per XCD g = 200000 over 100 us (2 GHz);
+    MFMA busy = 0.5 of g x 1024 SIMDs; busy CU cycles = 0.75 of g x 256 CUs."""
+    busy = tmp_path / "busy"
+    busy.mkdir()
+    _write_csv(busy / "run_agent_info.csv", ["Name", "Simd_Count", "Cu_Count", "Num_Xcc"],
+               [["gfx950", 1024, 256, 8]])
+    gemm = ("void mx::(anonymous namespace)::gemm_bf16_kernel<0, 4, true, false, 0, false, 256, "
+            "256, 2, 4>(mx::(anonymous namespace)::Args)")
+    _write_csv(busy / "run_kernel_trace.csv", ["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                                "End_Timestamp"],
+               [[1, gemm, 1000, 101000], [2, gemm, 200000, 300000], [3, "other", 0, 10]])
+    g = 200000.0
+    counters = {"SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * g * 1024, "SQ_BUSY_CYCLES": 1.0,
+                "SQ_BUSY_CU_CYCLES": 0.75 * g * 256, "GRBM_GUI_ACTIVE": g * 8,
+                "SQ_INSTS_MFMA": 0.5 * g * 1024 / 32}
+    rows = [[d, gemm, name, v] for d in (1, 2) for name, v in counters.items()]
+    rows += [[3, "other", "GRBM_GUI_ACTIVE", 5.0]]
+    _write_csv(busy / "run_counter_collection.csv",
+               ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    out = bench.summarize_busy(str(busy), prof_dir=str(tmp_path))
+    assert out["dispatches"] == 2
+    assert abs(out["clock_ghz"] - 2.0) < 1e-4
+    assert abs(out["mfma_util"] - 0.5) < 1e-4
+    assert abs(out["cu_busy"] - 0.75) < 1e-4
+    assert abs(out["mfma_busy_over_busy_cu"] - 0.5 / 0.75) < 1e-3
+    assert out["mfma_busy_cycles_per_inst"] == 32.0
+    assert (tmp_path / "mfma_util_gemm_fp8_fp4_4096x7168x2048.json").exists()
