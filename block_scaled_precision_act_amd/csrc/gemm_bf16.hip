@@ -67,6 +67,10 @@ constexpr int kBK = 64;          // K elements per stage
 constexpr int kRowBytes = 128;   // one decoded LDS row: 64 bf16
 constexpr int kGroupM = 8;
 constexpr int kParts = 3;        // sub-steps that stage the next K step (the fourth holds the barrier)
+// s_waitcnt operand that waits for every vector-memory access of the wavefront (vmcnt 0) and
+// for nothing else (expcnt and lgkmcnt at their maxima): vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[15:14] in the gfx9 encoding.
+constexpr int kVmcntZero = 0x0F70;
 
 struct Args {
   const uint8_t* a;
@@ -624,17 +628,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), wsr, off,
                                                  split * kTileBytes, kDeviceScope);
         }
-    // The barrier orders every wavefront's partial stores before thread 0's device-scope
-    // acquire-release increment: its release writes this XCD's L2 back, so the partial reaches
+    // Handoff order.  (1) Every wavefront waits until its own partial stores are complete
+    // (vmcnt 0: acknowledged by this XCD's L2).  A workgroup barrier alone does not wait for
+    // stores in flight, and thread 0's release below waits only for its own wavefront's.
+    // (2) The barrier: past it, every store of the workgroup has reached the L2.  (3) Thread 0's
+    // device-scope acquire-release increment: its release writes this XCD's L2 back (every
+    // wavefront's partial included, by (1)) before the counter changes, so the partial is in
     // the memory every XCD shares; its acquire (on the last workgroup) invalidates this CU's and
     // XCD's caches, so the loads below, ordered after it by the second barrier, see the other
-    // ranges' partials.  One such fence pair per workgroup: a device-scope fence writes back or
+    // range's partial.  One release/acquire per workgroup: a device-scope fence writes back or
     // invalidates a whole L2, far too costly to run in every wavefront.
     __shared__ uint32_t arrived;
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
     if (threadIdx.x == 0) {
-      const uint32_t before = __hip_atomic_fetch_add(p.counters + tile_id, 1u, __ATOMIC_ACQ_REL,
+      // Release, spelled out so that the increment waits for the write-back to complete: the
+      // device-scope release fence writes this XCD's L2 back, the wait lets it finish.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      const uint32_t before = __hip_atomic_fetch_add(p.counters + tile_id, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       // the last arrival leaves the counter at zero for the next call
       if (before == static_cast<uint32_t>(p.splits - 1))
         __hip_atomic_store(p.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

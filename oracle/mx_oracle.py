@@ -79,7 +79,7 @@ def e8m0_to_f64(scale_bytes) -> np.ndarray:
     s = np.asarray(scale_bytes, dtype=np.uint8)
     n_nan = int(np.count_nonzero(s == E8M0_NAN))
     if n_nan:
-        raise OracleRefusal(f"E8M0 scale holds {n_nan} NaN bytes (255)")
+        raise OracleRefusal(f"{n_nan} scale byte(s) equal 255, which E8M0 reserves for NaN")
     return np.ldexp(1.0, s.astype(np.int64) - 127)
 
 
@@ -131,7 +131,8 @@ def decode_fp4_rows(packed, scale_bytes) -> np.ndarray:
     R, K = codes.shape
     s = np.asarray(scale_bytes, dtype=np.uint8)
     if K % BLOCK or s.shape != (R, K // BLOCK):
-        raise OracleRefusal(f"fp4 {codes.shape} vs scale {s.shape}")
+        raise OracleRefusal(f"scales shaped {s.shape} do not give each of the {R} rows of {K} "
+                            f"E2M1 values one byte per {BLOCK} values")
     v = e2m1_to_f64(codes).reshape(R, K // BLOCK, BLOCK)
     return (v * e8m0_to_f64(s)[:, :, None]).reshape(R, K)
 
@@ -145,7 +146,8 @@ def decode_e4m3_rows(codes, scale_bytes) -> np.ndarray:
     R, K = c.shape
     s = np.asarray(scale_bytes, dtype=np.uint8)
     if K % BLOCK or s.shape != (R, K // BLOCK):
-        raise OracleRefusal(f"e4m3 rows {c.shape} vs scale {s.shape}")
+        raise OracleRefusal(f"scales shaped {s.shape} do not give each row of the {c.shape} "
+                            f"E4M3 codes one byte per {BLOCK} values")
     v = e4m3_to_f64(c).reshape(R, K // BLOCK, BLOCK)
     return (v * e8m0_to_f64(s)[:, :, None]).reshape(R, K)
 
@@ -161,7 +163,8 @@ def decode_fp8_block(codes, scale_bytes) -> np.ndarray:
     s = np.asarray(scale_bytes, dtype=np.uint8)
     nb, kb = -(-N // BLOCK), -(-K // BLOCK)
     if s.shape != (nb, kb):
-        raise OracleRefusal(f"fp8 {c.shape} vs block scale {s.shape}")
+        raise OracleRefusal(f"block scales shaped {s.shape} do not cover the {c.shape} E4M3 "
+                            f"weight in {BLOCK}x{BLOCK} blocks")
     scale = e8m0_to_f64(s)
     rows = np.arange(N) // BLOCK
     cols = np.arange(K) // BLOCK
