@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmx_gfx950.so")
 
-SOURCES = ["mx_api.cpp", "act_quant.hip", "quant_transpose.hip", "gemm_fp4.hip", "gemm_bf16.hip"]
+SOURCES = ["mx_api.cpp", "act_quant.hip", "quant_transpose.hip", "gemm_fp4.hip", "gemm_bf16.hip",
+           "gemm_mx.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -38,99 +38,14 @@
 //     bf16 values out.
 #include <atomic>
 
-#include "mx_epilogue.h"
-#include "mx_internal.h"
-#include "mx_quant.h"
+#include "gemm_common.h"
 
 namespace mx {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-template <int V>
-struct IntC { static constexpr int value = V; };
-
-// Calls f(IntC<I>{}) for I in [B, E), unrolled at compile time.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(IntC<B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 constexpr int kBK = 64;          // K elements per stage
 constexpr int kRowBytes = 128;   // one decoded LDS row: 64 bf16
-constexpr int kGroupM = 8;
 constexpr int kParts = 3;        // sub-steps that stage the next K step (the fourth holds the barrier)
-// s_waitcnt operand that waits for every vector-memory access of the wavefront (vmcnt 0) and
-// for nothing else (expcnt and lgkmcnt at their maxima): vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
-// vmcnt[15:14] in the gfx9 encoding.
-constexpr int kVmcntZero = 0x0F70;
-
-struct Args {
-  const uint8_t* a;
-  const uint8_t* a_s;
-  const uint8_t* b;
-  const uint8_t* b_s;
-  const uint16_t* bias;
-  uint16_t* c;
-  int M, N, K;
-  int tiles_m, tiles_n;
-  int64_t stride_a, stride_as, stride_b, stride_bs, stride_bias, stride_c;
-  uint8_t* q;
-  uint8_t* qs;
-  int64_t stride_q, stride_qs;
-  const uint16_t* res;
-  int64_t stride_res;
-  // SPLIT: K split into `splits` equal ranges of K steps per tile; fp32 partial tiles in `ws`
-  // (tile-major, then range), one arrival counter per tile in `counters` (zero between calls).
-  float* ws;
-  uint32_t* counters;
-  int splits;
-};
-
-// fp32 value of an E8M0 byte (2^(b-127)); byte 0 is the fp32 subnormal 2^-127.
-__device__ __forceinline__ float e8m0_value(uint32_t b) {
-  return __uint_as_float(max(b << 23, 0x00400000u));
-}
-
-__device__ __forceinline__ uint32_t pk_bits(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
-
-// 8 E2M1 codes (one dword, low nibble first) times s -> 8 bf16.
-__device__ __forceinline__ uint4 decode_fp4_dword(uint32_t d, float s) {
-  uint4 o;
-  o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0));
-  o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 1));
-  o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2));
-  o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 3));
-  return o;
-}
-
-// 8 E4M3 codes (two dwords) times s -> 8 bf16.
-__device__ __forceinline__ uint4 decode_fp8_pair(uint32_t lo, uint32_t hi, float s) {
-  uint4 o;
-  o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, false));
-  o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, s, true));
-  o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, false));
-  o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, s, true));
-  return o;
-}
-
-// 8 E5M2 codes (two dwords) times s -> 8 bf16.
-__device__ __forceinline__ uint4 decode_bf8_pair(uint32_t lo, uint32_t hi, float s) {
-  uint4 o;
-  o.x = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, s, false));
-  o.y = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(lo, s, true));
-  o.z = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, s, false));
-  o.w = pk_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(hi, s, true));
-  return o;
-}
-
 // Decoded rows are 128 B (64 bf16 = 8 chunks of 16 B).  Chunk c of row r is stored at chunk
 // c ^ swz(r), swz(r) = (r & 7) ^ parity(bits 1..3 of r), period 16 in r.  It keeps every LDS pass
 // free of bank conflicts, whether a pass serves 8 lanes (128 B of banks) or 16 lanes (256 B), for
@@ -152,12 +67,6 @@ __device__ __forceinline__ uint32_t lds_offset(int row, int chunk) {
 template <int FMT>
 __device__ __forceinline__ int graw(int row) {
   return byte_codes(FMT) ? (row >> 2) & 3 : (row >> 3) & 1;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  // Raw buffer (stride 0) with a byte bound: loads at or past `bytes` return zero.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
 }
 
 // Moves one operand's codes for one K step from global memory into an LDS stage region.
@@ -224,7 +133,9 @@ struct Stager {
     raw[I] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(codes, v, kt * kStepBytes, 0));
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (DECODE) {
-      sbyte[I] = __builtin_amdgcn_raw_buffer_load_b8(scales, soff[I], kt * 2, 0);
+      // the scale byte of a 32-block past K (upper half of a last half step) is not read
+      sbyte[I] = __builtin_amdgcn_raw_buffer_load_b8(scales, (partial && upper) ? kOob : soff[I],
+                                                     kt * 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -334,9 +245,13 @@ struct BRegs {
     }
   }
 
-  __device__ __forceinline__ void load_scales(int kt) {
+  // Scale bytes of step kt; `partial`: a last half step, whose second 32-block (lane group 1)
+  // is past K and is not read.
+  __device__ __forceinline__ void load_scales(int kt, bool partial) {
+    const bool skip = partial && (threadIdx.x & 32) != 0;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sbyte[j] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, soff[j], kt * 2, 0);
+    for (int j = 0; j < TN; ++j)
+      sbyte[j] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, skip ? 0x80000000u : soff[j], kt * 2, 0);
   }
 
   __device__ __forceinline__ void take_scales() {
@@ -375,19 +290,6 @@ struct BRegs {
     static_for<0, TN>([&](auto jc) { decode<S, decltype(jc)::value>(out[decltype(jc)::value]); });
   }
 };
-
-// Tile coordinates of workgroup `bid` out of `nb`: XCD-contiguous, then grouped by kGroupM rows.
-__device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
-  int id = bid;
-  if ((nb & 7) == 0) id = (bid & 7) * (nb >> 3) + (bid >> 3);
-  const int per_group = kGroupM * tiles_n;
-  const int g = id / per_group;
-  const int first_m = g * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_g = id - g * per_group;
-  tm = first_m + in_g % gsize;
-  tn = in_g / gsize;
-}
 
 template <int TM>
 __device__ __forceinline__ void read_a(const uint8_t* stage, uint32_t a_base, uint32_t coff,
@@ -471,9 +373,9 @@ __device__ __forceinline__ void k_step(const uint8_t* cur, uint8_t* nxt, uint32_
 // EPI (bf16 output only): kEpiResidual adds the bf16 residual [M, N] before the rounding,
 // kEpiGelu applies GELU to (sum + bias); both take the bias pointer as optional (BIAS is true
 // for them and a null bias adds nothing).
-// SPLIT (splits == 2): workgroup b computes K range (b % 2) of tile b / 2 and stores its fp32
-// partial tile; the workgroup that arrives second at the tile's counter (no workgroup ever waits
-// for another) adds the other partial to its own and runs the epilogue.
+// SPLIT (splits == 2): workgroup b computes K range (b % 2) of tile b / 2; the first of the two to
+// finish publishes its fp32 partial tile, the second adds it to its own and runs the epilogue
+// (finish_tile).
 // LDS of one workgroup: the two operand stages, reused by the bf16 output tile of the epilogue,
 // then the tile's bias as fp32.
 template <int AF, int BF, int BM, int BN>
@@ -567,7 +469,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   const int last_partial = (p.K % kBK) != 0 ? KT_all - 1 : -1;
   sa.load_all(k0, last_partial == k0);
   sb.load_all(k0, last_partial == k0);
-  br.load_scales(k0);
+  br.load_scales(k0, last_partial == k0);
   sa.store_all(lds);
   sb.store_all(lds);
   if (KT > 1) {
@@ -587,13 +489,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   });
   br.read_raw_all(lds);
   br.template decode_all<0>(fb[0]);
-  if (KT > 1) br.load_scales(k0 + 1);
+  if (KT > 1) br.load_scales(k0 + 1, last_partial == k0 + 1);
 
   int kt = 0;
   for (; kt + 2 < KT; ++kt) {
     k_step<true, true>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes, a_base,
                        coff, sa, sb, br, fa, fb, acc, k0 + kt + 2, k0 + kt + 2 == last_partial);
-    br.load_scales(k0 + kt + 2);
+    br.load_scales(k0 + kt + 2, last_partial == k0 + kt + 2);
   }
   if (kt + 1 < KT) {
     k_step<true, false>(lds + (kt & 1) * kStageBytes, lds + ((kt + 1) & 1) * kStageBytes, a_base,
@@ -603,240 +505,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Args p) {
   k_step<false, false>(lds + (kt & 1) * kStageBytes, lds, a_base, coff, sa, sb, br, fa, fb, acc,
                        0, false);
 
-  if constexpr (SPLIT) {
-    // This range's partial tile: thread t's accumulator values as 16-byte units u at
-    // (u * NT + t), so every store and load below is one coalesced 1 KB row per wavefront.
-    // The partials are stored and loaded with device-scope cache policy (sc1): written through
-    // to the memory every XCD shares instead of sitting dirty in this XCD's L2, so the release
-    // below has little to write back.
-    constexpr int kUnits = TM * TN * 4;
-    constexpr uint32_t kTileBytes = static_cast<uint32_t>(kUnits) * NT * 16;
-    constexpr int kDeviceScope = 16;     // the sc1 cache-policy bit
-    const __amdgpu_buffer_rsrc_t wsr = make_rsrc(
-        reinterpret_cast<const uint8_t*>(p.ws) + static_cast<int64_t>(tile_id) * p.splits * kTileBytes,
-        kTileBytes * static_cast<uint32_t>(p.splits));
-    const uint32_t lane_off = threadIdx.x * 16u;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t off = static_cast<uint32_t>(((i * TN + j) * 4 + q) * NT * 16) + lane_off;
-          const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                         acc[i][j][4 * q + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), wsr, off,
-                                                 split * kTileBytes, kDeviceScope);
-        }
-    // Handoff order.  (1) Every wavefront waits until its own partial stores are complete
-    // (vmcnt 0: acknowledged by this XCD's L2).  A workgroup barrier alone does not wait for
-    // stores in flight, and thread 0's release below waits only for its own wavefront's.
-    // (2) The barrier: past it, every store of the workgroup has reached the L2.  (3) Thread 0's
-    // device-scope acquire-release increment: its release writes this XCD's L2 back (every
-    // wavefront's partial included, by (1)) before the counter changes, so the partial is in
-    // the memory every XCD shares; its acquire (on the last workgroup) invalidates this CU's and
-    // XCD's caches, so the loads below, ordered after it by the second barrier, see the other
-    // range's partial.  One release/acquire per workgroup: a device-scope fence writes back or
-    // invalidates a whole L2, far too costly to run in every wavefront.
-    __shared__ uint32_t arrived;
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      // Release, spelled out so that the increment waits for the write-back to complete: the
-      // device-scope release fence writes this XCD's L2 back, the wait lets it finish.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      const uint32_t before = __hip_atomic_fetch_add(p.counters + tile_id, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      // the last arrival leaves the counter at zero for the next call
-      if (before == static_cast<uint32_t>(p.splits - 1))
-        __hip_atomic_store(p.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      arrived = before;
-    }
-    __syncthreads();
-    if (arrived != static_cast<uint32_t>(p.splits - 1)) return;   // not the last: done
-    // Two ranges: the tile is own + other, and fp32 addition is commutative, so the sum is the
-    // same bits whichever workgroup arrives last.
-    const int other = 1 - split;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t off = static_cast<uint32_t>(((i * TN + j) * 4 + q) * NT * 16) + lane_off;
-          const v4f v = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    wsr, off, other * kTileBytes, kDeviceScope));
-          acc[i][j][4 * q] += v[0];
-          acc[i][j][4 * q + 1] += v[1];
-          acc[i][j][4 * q + 2] += v[2];
-          acc[i][j][4 * q + 3] += v[3];
-        }
-  }
-
-  // Epilogue, staged through LDS: fp32 + bias, one bf16 rounding, written into a row-major bf16
-  // tile [BM][BN], then copied out in coalesced 16-byte row segments.  The MFMA takes B as its
-  // first operand, so accumulator block (i, j) holds C^T: element 4 r4 + k of a lane is row
-  // 32 i + l32 and column 32 j + 8 r4 + 4 h + k of the wavefront tile, four consecutive
-  // columns of one row, written to LDS as one 8-byte store.  16-byte chunk c of tile row r sits
-  // at chunk c ^ tile_ch(r): the 16 rows that 16 lanes write in one pass land in 16 different
-  // 16-byte bank groups, and a row's chunks stay a permutation of themselves for the copy-out.
-  __syncthreads();                       // every wavefront is done reading the operand stages
-  constexpr int kTileRow = BN * 2;       // bytes of one bf16 tile row
-  constexpr int kChunksPerRow = BN / 8;
-  auto tile_ch = [](int r, int c) {
-    return kChunksPerRow >= 16 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
-  };
-  if constexpr (EPI == kEpiResidual) {
-    // The residual tile is first copied into the LDS tile in the same layout, with coalesced
-    // 16-byte loads (zeros outside the matrix); each thread below reads the residual at its own
-    // outputs' places and overwrites them with the results.  The residual may be the output
-    // itself: every read of the tile precedes the barrier before the copy-out.
-    const uint16_t* res = p.res + bz * p.stride_res;
-    constexpr int kResStep = NT / kChunksPerRow;   // rows between a thread's chunks
-    constexpr int kResIters = BM / kResStep;
-    static_assert(NT % kChunksPerRow == 0 && BM % kResStep == 0, "residual rows");
-    if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
-        (reinterpret_cast<uintptr_t>(res) & 15u) == 0) {
-      // A tile inside a residual whose rows are 16-byte aligned: every thread loads its chunk
-      // column of all the tile's rows before storing any of it, so the loads are in flight
-      // together instead of one memory round trip per chunk.
-      const int trow0 = threadIdx.x / kChunksPerRow, tch = threadIdx.x % kChunksPerRow;
-      const uint16_t* src = res + static_cast<int64_t>(m0 + trow0) * p.N + n0 + tch * 8;
-      const int64_t step = static_cast<int64_t>(kResStep) * p.N;
-      uint4 v[kResIters];
-#pragma unroll
-      for (int it = 0; it < kResIters; ++it) v[it] = *reinterpret_cast<const uint4*>(src + it * step);
-#pragma unroll
-      for (int it = 0; it < kResIters; ++it) {
-        const int trow = trow0 + it * kResStep;
-        *reinterpret_cast<uint4*>(lds + trow * kTileRow + tile_ch(trow, tch) * 16) = v[it];
-      }
-    } else {
-      for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-        const int row = m0 + trow, col = n0 + tch * 8;
-        const int ch = tile_ch(trow, tch);
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (row < p.M && col < p.N) {
-          const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
-          if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-            v = *reinterpret_cast<const uint4*>(src);
-          } else {
-            uint32_t e[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) e[k] = col + k < p.N ? src[k] : 0u;
-            v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                      e[6] | (e[7] << 16)};
-          }
-        }
-        *reinterpret_cast<uint4*>(lds + trow * kTileRow + ch * 16) = v;
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int tcol = wn * WTN + 32 * j + 8 * r4 + 4 * h;        // columns tcol .. tcol + 3
-      v4f bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (has_bias)
-        bias4 = *reinterpret_cast<const v4f*>(lds_bias + tcol);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int trow = wm * WTM + 32 * i + l32;
-        const uint32_t off = static_cast<uint32_t>(trow * kTileRow + tile_ch(trow, tcol >> 3) * 16 +
-                                                   (tcol & 7) * 2);
-        float v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * r4 + k] + bias4[k];
-        if constexpr (EPI == kEpiResidual) {
-          const uint2 r = *reinterpret_cast<const uint2*>(lds + off);
-          v[0] += bf16_bits_to_f32(r.x & 0xFFFFu);
-          v[1] += bf16_bits_to_f32(r.x >> 16);
-          v[2] += bf16_bits_to_f32(r.y & 0xFFFFu);
-          v[3] += bf16_bits_to_f32(r.y >> 16);
-        } else if constexpr (EPI == kEpiGelu) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = gelu_f32(v[k]);
-        }
-        const bf16x2 lo = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])};
-        const bf16x2 hi = {static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
-        *reinterpret_cast<uint2*>(lds + off) = uint2{pk_bits(lo), pk_bits(hi)};
-      }
-    }
-  }
-  __syncthreads();
-  if constexpr (QUANT) {
-    // Four consecutive lanes hold the four 16-byte chunks of one 32-column block of a row
-    // (kChunksPerRow % 4 == 0), and every lane of the workgroup runs every iteration (the tile's
-    // chunk count is a multiple of the workgroup size), so the quad permutes only mix live lanes.
-    // N % 32 == 0: a block is entirely inside or entirely outside the matrix.
-    static_assert(kChunksPerRow % 4 == 0 && (BM * kChunksPerRow) % NT == 0, "quad blocks");
-    uint8_t* q = p.q + bz * p.stride_q;
-    uint8_t* qs = p.qs + bz * p.stride_qs;
-    const int nb = p.N / 32;
-    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-      const int row = m0 + trow, col = n0 + tch * 8;
-      const int ch = tile_ch(trow, tch);
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
-      if constexpr (AF == kFp4) {
-        const QuantChunkFp4 qc = quant_chunk_fp4(v);
-        if (row < p.M && col < p.N) {
-          *reinterpret_cast<uint32_t*>(q + static_cast<int64_t>(row) * (p.N / 2) + col / 2) = qc.codes;
-          if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
-        }
-      } else {
-        const QuantChunk qc = quant_chunk(v);
-        if (row < p.M && col < p.N) {
-          *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row) * p.N + col) = qc.codes;
-          if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
-        }
-      }
-    }
-  } else {
-    uint16_t* c = p.c + bz * p.stride_c;
-    // A tile wholly inside an output whose rows are 16-byte aligned: every thread copies the same
-    // chunk column of rows trow0 + kRowStep * it, all LDS reads issued before the stores.
-    constexpr int kRowStep = NT / kChunksPerRow;
-    constexpr int kIters = BM / kRowStep;
-    static_assert(NT % kChunksPerRow == 0 && kRowStep % 16 == 0 && BM % kRowStep == 0,
-                  "copy-out rows keep their chunk swizzle");
-    if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
-        (reinterpret_cast<uintptr_t>(c) & 15u) == 0) {
-      const int trow0 = threadIdx.x / kChunksPerRow, tch = threadIdx.x % kChunksPerRow;
-      const uint8_t* src = lds + trow0 * kTileRow + tile_ch(trow0, tch) * 16;
-      uint4 v[kIters];
-#pragma unroll
-      for (int it = 0; it < kIters; ++it)
-        v[it] = *reinterpret_cast<const uint4*>(src + it * kRowStep * kTileRow);
-      uint16_t* dst = c + static_cast<int64_t>(m0 + trow0) * p.N + n0 + tch * 8;
-      const int64_t step = static_cast<int64_t>(kRowStep) * p.N;
-#pragma unroll
-      for (int it = 0; it < kIters; ++it) *reinterpret_cast<uint4*>(dst + it * step) = v[it];
-    } else {
-      for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-        const int row = m0 + trow, col = n0 + tch * 8;
-        if (row >= p.M || col >= p.N) continue;
-        const int ch = tile_ch(trow, tch);
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + trow * kTileRow + ch * 16);
-        uint16_t* dst = c + static_cast<int64_t>(row) * p.N + col;
-        if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-          *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
-            if (col + k < p.N) dst[k] = static_cast<uint16_t>((k & 1) ? w >> 16 : w);
-          }
-        }
-      }
-    }
-  }
+  finish_tile<AF, QUANT, EPI, SPLIT, BM, BN, WM, WN>(
+      p, acc, [&](int r) { return lds + r * (BN * 2); }, lds_bias, has_bias, split, tile_id, m0, n0,
+      bz);
 }
 
 
@@ -885,8 +556,8 @@ hipError_t launch_tile(const GemmProblem& g, int device, hipStream_t stream) {
 }
 
 // Split-K launch: 256x256 tiles, grid = tiles * splits (one batch), bf16 output with an optional
-// bias.  The workspace holds the tile counters (zero on entry, left zero on exit) and then the
-// fp32 partial tiles.
+// bias.  The workspace holds a counter and a ready flag per tile (zero on entry, left zero on
+// exit) and then one fp32 partial tile per tile.
 template <int AF, int BF>
 hipError_t launch_split(const GemmProblem& g, const SplitPlan& plan, int device,
                          hipStream_t stream) {
@@ -907,7 +578,10 @@ template <int AF, int BF>
 hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream_t stream) {
   if (g.workspace) {
     const SplitPlan plan = plan_split(g.M, g.N, g.K, g.batch);
-    if (plan.splits > 1) return launch_split<AF, BF>(g, plan, dev.device, stream);
+    if (plan.splits > 1) {
+      if (mx_kernel_takes(g.K, plan.splits)) return launch_gemm_mx(AF, BF, g, &plan, stream);
+      return launch_split<AF, BF>(g, plan, dev.device, stream);
+    }
   }
   // Largest tile that still gives every CU a workgroup; the smallest one otherwise.
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
@@ -919,7 +593,10 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   // finishing them as 256 tiles of 256x192 in a second launch measured the same total time.
   // Above half the CUs, one wave of 256x256 tiles beats the three or four waves of 128x128 tiles
   // the same output needs (a 128x128 step costs 0.37 of a 256x256 step for a quarter of the work).
-  if (2 * tiles(256, 256) > cus) return launch_tile<AF, BF, 256, 256, 2, 4>(g, dev.device, stream);
+  if (2 * tiles(256, 256) > cus) {
+    if (mx_kernel_takes(g.K, 1)) return launch_gemm_mx(AF, BF, g, nullptr, stream);
+    return launch_tile<AF, BF, 256, 256, 2, 4>(g, dev.device, stream);
+  }
   if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, dev.device, stream);
   return launch_tile<AF, BF, 64, 64, 2, 2>(g, dev.device, stream);
 }

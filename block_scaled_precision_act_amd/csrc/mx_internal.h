@@ -45,13 +45,14 @@ struct GemmProblem {
 
 // Split-K plan of the tiled kernel for problems with fewer 256x256 output tiles than the 256 CUs
 // of an MI355X and a long K (large down-projections): K is cut into two equal ranges of 64-wide
-// steps, each range of each tile is one workgroup, and the second workgroup to finish a tile
-// adds the other's fp32 partial tile to its own.  Only single problems (batch 1) with 65..128
-// tiles (where the unsplit launch needs two or more waves of 128x128 tiles) and at least 40 steps
-// per range: elsewhere the partial tiles' traffic (256 KB written and read per tile, through one
-// CU) cost more than the idle CUs did (measured).  The plan depends on the shape alone, so the workspace size a caller
-// asks for is the one the launch uses.  Workspace: `counter_bytes` of per-tile counters (zero
-// between calls), then tiles * 2 partial tiles of 256 * 256 fp32.
+// steps, each range of each tile is one workgroup, and the first workgroup to finish a tile
+// publishes its fp32 partial tile for the second, which adds it to its own.  Only single
+// problems (batch 1) with 65..128 tiles (where the unsplit launch needs two or more waves of
+// 128x128 tiles) and at least 40 steps per range: elsewhere the partial tiles' traffic (256 KB
+// written and read per tile, through one CU) cost more than the idle CUs did (measured).  The
+// plan depends on the shape alone, so the workspace size a caller asks for is the one the launch
+// uses.  Workspace: `counter_bytes` holding a counter and a ready flag per tile (zero between
+// calls), then one partial tile of 256 * 256 fp32 per tile.
 struct SplitPlan {
   int splits = 1;
   int64_t counter_bytes = 0;
@@ -60,6 +61,7 @@ struct SplitPlan {
 constexpr int64_t kSplitTargetCUs = 256;
 constexpr int64_t kMinSplitTiles = 65;
 constexpr int64_t kMinStepsPerSplit = 40;
+constexpr int64_t kSplitTileBytes = 256 * 256 * 4;
 
 inline SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t batch) {
   SplitPlan p;
@@ -68,10 +70,9 @@ inline SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t batch) {
   const int64_t steps = (K + 63) / 64;
   if (2 * tiles > kSplitTargetCUs || tiles < kMinSplitTiles || steps < 2 * kMinStepsPerSplit)
     return p;
-  const int64_t s = 2;
-  p.splits = static_cast<int>(s);
-  p.counter_bytes = (tiles * 4 + 255) / 256 * 256;
-  p.bytes = p.counter_bytes + tiles * s * 256 * 256 * 4;
+  p.splits = 2;
+  p.counter_bytes = (tiles * 8 + 255) / 256 * 256;
+  p.bytes = p.counter_bytes + tiles * kSplitTileBytes;
   return p;
 }
 
@@ -100,6 +101,15 @@ hipError_t launch_quant_transpose(const uint16_t* x, uint8_t* q, uint8_t* s, int
 // FP8-operand kinds: exact bf16 decode + bf16 MFMA (gemm_bf16.hip).
 hipError_t launch_gemm_bf16(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
                             hipStream_t stream);
+// The same GEMMs on 256x256 tiles with one wavefront per SIMD and operands staged raw into LDS
+// by direct-to-LDS loads (gemm_mx.hip); `plan` non-null: split-K with p.workspace.  It runs K in
+// loop iterations of 8 steps of 64 (and reads scale bytes 4 steps at a time with 8-byte loads),
+// so it takes K % 512 == 0, and for a split, ranges of a multiple of 8 steps.
+inline bool mx_kernel_takes(int64_t K, int splits) {
+  return K > 0 && K % 512 == 0 && ((K / 64) % (8 * splits)) == 0;
+}
+hipError_t launch_gemm_mx(int a_fmt, int b_fmt, const GemmProblem& p, const SplitPlan* plan,
+                          hipStream_t stream);
 // Both operands MXFP4 on the scaled f8f6f4 MFMA (gemm_fp4.hip).
 hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream);
 

@@ -361,10 +361,13 @@ int mx_gemm_fp4_fp4_bias_gelu_strided_batched(const void* a, const void* a_scale
  * large down-projection shapes (API list; the paragraph after the schedule variants).  Here the
  * load-balancing variant splits K: a single problem with 65..128 output tiles of 256 x 256
  * (fewer than the 256 CUs of an MI355X) and at least 80 K steps of 64 has each tile's K cut into
- * 2 equal ranges computed by separate workgroups; each stores its fp32 partial tile in the
- * workspace, and the workgroup that finishes a tile last adds the partials in range order (the
- * same order on every run, so results are reproducible), adds the bias and rounds once to bf16.
- * No workgroup waits for another.  Shapes the plan does not split (the skinny MXFP4 x MXFP4
+ * 2 equal ranges computed by separate workgroups.  The first of the two to finish stores its
+ * fp32 partial tile in the workspace and raises the tile's ready flag; the other waits for the
+ * flag (only ever for a workgroup that is already running and waits for nothing), adds that
+ * partial to its own (fp32 addition commutes, so the bits do not depend on which came first),
+ * adds the bias and rounds once to bf16.  A wait past about 2^22 polls, which no working device
+ * reaches, gives up and writes NaN for that tile instead of hanging.  Shapes the plan does not
+ * split (the skinny MXFP4 x MXFP4
  * shapes, M <= 64, among them) run exactly as mx_gemm_<kind>_bias (or without bias) do, and
  * need no workspace.
  *
@@ -373,8 +376,9 @@ int mx_gemm_fp4_fp4_bias_gelu_strided_batched(const void* a, const void* a_scale
  * mx_gemm_<kind>_splitk: as mx_gemm_<kind>_bias with bias optional (NULL: no bias), single
  *   problem, plus
  *   workspace        device memory of at least the size above, 256-byte aligned; before its
- *                    first use it must be zero-filled (its head holds per-tile counters); every
- *                    completed call leaves those counters zero again, so it can be reused as is.
+ *                    first use it must be zero-filled (its head holds a counter and a ready flag
+ *                    per tile); every completed call leaves them zero again, so it can be reused
+ *                    as is.  The rest holds one fp32 256 x 256 partial tile per output tile.
  *                    Calls sharing one workspace must not run concurrently.
  *   workspace_bytes  its size.  MX_ERR_WORKSPACE when a split shape gets a NULL, smaller or
  *                    misaligned workspace.

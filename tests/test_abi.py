@@ -218,9 +218,10 @@ def test_size_limit_is_enforced(lib):
 
 def test_splitk_workspace_size_plan():
     # 256x256 tiles; two K ranges when there are 65..128 tiles and >= 80 K steps of 64;
-    # workspace = per-tile counters (rounded up to 256 B) + tiles * 2 fp32 tiles.
+    # workspace = a counter and a ready flag per tile (rounded up to 256 B) + one fp32 partial
+    # tile per output tile.
     def size(tiles):
-        return ((tiles * 4 + 255) // 256) * 256 + tiles * 2 * 256 * 256 * 4
+        return ((tiles * 8 + 255) // 256) * 256 + tiles * 256 * 256 * 4
     assert mx.mx_gemm_splitk_workspace_size(4096, 2048, 7168) == size(128)
     assert mx.mx_gemm_splitk_workspace_size(2000, 4000, 5152) == size(128)
     assert mx.mx_gemm_splitk_workspace_size(1280, 3328, 5120) == size(65)

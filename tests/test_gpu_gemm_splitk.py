@@ -26,8 +26,9 @@ def _workspace(mx, M, N, K):
 
 
 def _counters_zero(ws, M, N):
+    """Counters and ready flags (one each per tile) back at zero."""
     tiles = -(-M // 256) * -(-N // 256)
-    return int(ws[:tiles * 4].count_nonzero()) == 0
+    return int(ws[:tiles * 8].count_nonzero()) == 0
 
 
 def _operands(kind, M, N, K, seed, with_bias):
@@ -128,7 +129,7 @@ def test_first_call_on_fresh_workspace_with_garbage_partials(mx, kind):
     n = mx.mx_gemm_splitk_workspace_size(M, N, K)
     tiles = -(-M // 256) * -(-N // 256)
     ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
-    ws[:tiles * 4].zero_()
+    ws[:tiles * 8].zero_()
     torch.cuda.synchronize()
     note(f"gemm splitk {kind} {M}x{N}x{K} fresh workspace, garbage partials")
     out = _run(mx, kind, a, a_s, w, ws, M, N)
@@ -201,4 +202,4 @@ def test_concurrent_streams_give_single_stream_bytes(mx):
         for i, (g, r) in enumerate(zip(got, ref)):
             assert np.array_equal(g, r), (rep, i)
         for t in ins:
-            assert int(t[5][:65 * 4].count_nonzero()) == 0
+            assert int(t[5][:65 * 8].count_nonzero()) == 0

@@ -25,6 +25,7 @@ def _stats_kernel_names():
 
 
 def test_every_kernel_pattern_names_a_profiled_kernel():
+    # the kernels of a default run, in the kernel-trace summary of a default run
     names = _stats_kernel_names()
     assert names, "no kernel-trace summary under profiles/"
     for pattern in bench.KERNEL_PATTERNS:
@@ -59,8 +60,8 @@ def test_summarize_busy_arithmetic(tmp_path):
     busy.mkdir()
     _write_csv(busy / "run_agent_info.csv", ["Name", "Simd_Count", "Cu_Count", "Num_Xcc"],
                [["gfx950", 1024, 256, 8]])
-    gemm = ("void mx::(anonymous namespace)::gemm_bf16_kernel<0, 4, true, false, 0, false, 256, "
-            "256, 2, 4>(mx::(anonymous namespace)::Args)")
+    gemm = ("void mx::(anonymous namespace)::gemm_mx_kernel<0, 4, true, false, 0, false>"
+            "(mx::(anonymous namespace)::Args)")
     _write_csv(busy / "run_kernel_trace.csv", ["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
                                                 "End_Timestamp"],
                [[1, gemm, 1000, 101000], [2, gemm, 200000, 300000], [3, "other", 0, 10]])
