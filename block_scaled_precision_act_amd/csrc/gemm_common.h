@@ -318,7 +318,11 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
     uint8_t* q = p.q + bz * p.stride_q;
     uint8_t* qs = p.qs + bz * p.stride_qs;
     const int nb = p.N / 32;
-    for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+    // a fixed trip count, unrolled, so that several iterations' LDS reads are in flight together
+    constexpr int kQIters = BM * kChunksPerRow / NT;
+#pragma unroll 8
+    for (int it = 0; it < kQIters; ++it) {
+      const int idx = static_cast<int>(threadIdx.x) + it * NT;
       const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
       const int row = m0 + trow, col = n0 + tch * 8;
       const int ch = tile_ch(trow, tch);
