@@ -58,6 +58,7 @@ for _n in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
                                                         _I, _I, _I, _I, _I, _I, _P]
     _SIGS[f"mx_gemm_{_n}_splitk"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _P]
 _SIGS["mx_gemm_splitk_workspace_size"] = [_I, _I, _I]
+_SIGS["mx_gemm_fp8_fp4_splitk_noalloc"] = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]
 _U64, _C = ctypes.c_uint64, ctypes.c_int
 _SIGS["mx_quant_e5m2"] = [_P, _P, _P, _I, _I, _C, _U64, _P]
 _SIGS["mx_quant_e5m2_strided_batched"] = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _C, _U64, _P]
@@ -501,6 +502,21 @@ def mx_gemm_fp8_fp4_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None)
     output tiles; workspace: a zero-filled device buffer of mx_gemm_splitk_workspace_size bytes
     (256-byte aligned; left reusable), or None for shapes that are not split."""
     _gemm_splitk("fp8_fp4", a, a_s, b, b_s, c, workspace, bias, stream)
+
+
+def mx_gemm_fp8_fp4_splitk_noalloc(a, a_s, b, b_s, c, bias=None, stream=None):
+    """As mx_gemm_fp8_fp4_splitk without a workspace: the library's fixed device array holds the
+    partial tiles (calls on one GPU must not overlap)."""
+    M, N = c.shape
+    K = _k_of("fp8_fp4", a)
+    fn = "mx_gemm_fp8_fp4_splitk_noalloc"
+    dev = _current_device()
+    _need(fn, c, "c", "bf16", M, N, dev=dev)
+    _need_operands(fn, "fp8_fp4", a, a_s, b, b_s, M, N, K, None, dev=dev)
+    _need_bias(fn, bias, N, None, dev=dev)
+    _check(fn, load().mx_gemm_fp8_fp4_splitk_noalloc(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
+                                                     _ptr(bias), _ptr(c), M, N, K,
+                                                     _stream(stream)))
 
 
 def mx_gemm_fp8_fp8_splitk(a, a_s, b, b_s, c, workspace, bias=None, stream=None):

@@ -139,6 +139,8 @@ struct GemmCall {
   bool splitk = false;
   void* ws = nullptr;
   int64_t ws_bytes = 0;
+  // Split-K on the library's own device array (the _splitk_noalloc entry point).
+  bool no_alloc = false;
 };
 
 int validate_gemm(const GemmCall& g) {
@@ -161,6 +163,10 @@ int validate_gemm(const GemmCall& g) {
     if (plan.splits > 1 && (!g.ws || g.ws_bytes < plan.bytes ||
                             (reinterpret_cast<uintptr_t>(g.ws) & 255u) != 0))
       return MX_ERR_WORKSPACE;
+  }
+  if (g.no_alloc) {
+    const mx::SplitPlan plan = mx::plan_split(g.M, g.N, g.K, g.batch);
+    if (plan.splits > 1 && plan.bytes > mx::no_alloc_scratch_bytes()) return MX_ERR_WORKSPACE;
   }
   if (g.epi == mx::kEpiResidual && !g.res) return MX_ERR_NULL;
   if (!mx::aligned16(g.a) || !mx::aligned16(g.b)) return MX_ERR_ALIGN;
@@ -202,7 +208,9 @@ int gemm_impl(const GemmCall& g, void* stream) {
     p.stride_q = g.sq;
     p.stride_qs = g.sqs;
   }
-  hipError_t e = mx::launch_gemm(g.a_fmt, g.b_fmt, p, dev, static_cast<hipStream_t>(stream));
+  hipError_t e = g.no_alloc
+      ? mx::launch_gemm_no_alloc(g.a_fmt, g.b_fmt, p, dev, static_cast<hipStream_t>(stream))
+      : mx::launch_gemm(g.a_fmt, g.b_fmt, p, dev, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
@@ -491,6 +499,14 @@ int64_t mx_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K) {
                                     workspace, workspace_bytes),                              \
                      stream);                                                                 \
   }
+
+int mx_gemm_fp8_fp4_splitk_noalloc(const void* a, const void* a_s, const void* b,
+                                   const void* b_s, const void* bias, void* c, int64_t M,
+                                   int64_t N, int64_t K, void* stream) {
+  GemmCall g = single(mx::kFp8, mx::kFp4, a, a_s, b, b_s, bias, c, M, N, K, false);
+  g.no_alloc = true;
+  return gemm_impl(g, stream);
+}
 
 MX_GEMM_SPLITK_ENTRY_POINT(fp8_fp4, mx::kFp8, mx::kFp4)
 MX_GEMM_SPLITK_ENTRY_POINT(fp8_fp8, mx::kFp8, mx::kFp8)

@@ -113,6 +113,13 @@ hipError_t launch_gemm_mx(int a_fmt, int b_fmt, const GemmProblem& p, const Spli
 // Both operands MXFP4 on the scaled f8f6f4 MFMA (gemm_fp4.hip).
 hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream);
 
+// The split GEMM of p on this library's fixed device array instead of p.workspace (which it
+// ignores), for callers that cannot allocate (gemm_scratch.hip); no_alloc_scratch_bytes() is the
+// array's size.
+hipError_t launch_gemm_no_alloc(int a_fmt, int b_fmt, GemmProblem p, const DeviceInfo& dev,
+                                hipStream_t stream);
+int64_t no_alloc_scratch_bytes();
+
 // Picks the kernel for a problem.
 hipError_t launch_gemm(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
                        hipStream_t stream);

@@ -395,6 +395,21 @@ int mx_gemm_fp4_fp4_splitk(const void* a, const void* a_scale, const void* b, co
                            const void* bias, void* c, int64_t M, int64_t N, int64_t K,
                            void* workspace, int64_t workspace_bytes, void* stream);
 
+/* mx_gemm_fp8_fp4_splitk_noalloc: mx_gemm_fp8_fp4_splitk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same kernels and results (bit for bit), and no
+ * allocation of any kind.  The counters, ready flags and partial tiles live in a fixed device
+ * array of this library, 32 MB + 1 KB, which every GPU the library runs on holds until the
+ * process ends; it covers every shape the split plan splits (at most 128 output tiles), and a
+ * plan that needed more would get MX_ERR_WORKSPACE.  Each call first clears the counters and
+ * flags it uses with a small fill kernel on `stream`, then launches the GEMM; shapes that are
+ * not split run as mx_gemm_fp8_fp4_bias (or without bias) and touch no array.  All calls on one
+ * GPU share its array and it keeps the last call's contents, so calls that overlap on one GPU
+ * (on concurrent streams, or from several threads) race: serialize them. */
+int mx_gemm_fp8_fp4_splitk_noalloc(const void* a, const void* a_scale, const void* b,
+                                   const void* b_scale, const void* bias, void* c, int64_t M,
+                                   int64_t N, int64_t K, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Backward-pass operands and GEMM (E5M2 gradients).
  *

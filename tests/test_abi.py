@@ -42,6 +42,7 @@ def test_header_declares_the_full_boundary():
     for k in ("fp8_fp4", "fp8_fp8", "fp4_fp4"):
         assert f"mx_gemm_{k}_splitk" in names
     assert "mx_gemm_splitk_workspace_size" in names
+    assert "mx_gemm_fp8_fp4_splitk_noalloc" in names
     for n in ("mx_quant_e5m2", "mx_quant_e5m2_strided_batched", "mx_quant_transpose_e4m3",
               "mx_quant_transpose_e5m2", "mx_gemm_e5m2_e4m3", "mx_gemm_e5m2_e4m3_strided_batched",
               "mx_gemm_e5m2_e4m3_splitk", "mx_gemm_fp4_fp4_quant",
@@ -51,7 +52,7 @@ def test_header_declares_the_full_boundary():
         for v in ("_bias_gelu_quant", "_bias_gelu_quant_strided_batched"):
             assert f"mx_gemm_{k}{v}" in names
     assert "mx_capability" in names and "mx_status_str" in names
-    assert len(names) == 53
+    assert len(names) == 54
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -317,3 +318,14 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mx.load(str(tmp_path / "missing.so"))
     finally:
         mx._lib = saved
+
+
+def test_splitk_noalloc_argument_errors(lib):
+    # a, a_s, b, b_s, bias (may be NULL), c, M, N, K: refused on the host before any HIP call
+    f = lib.mx_gemm_fp8_fp4_splitk_noalloc
+    assert f(A16, A16, A16, A16, None, A16, 16, 64, 48, None) == mx.MX_ERR_SHAPE     # K % 32
+    assert f(A16, A16, A16, A16, None, None, 16, 64, 64, None) == mx.MX_ERR_NULL     # c
+    assert f(None, A16, A16, A16, None, A16, 16, 64, 64, None) == mx.MX_ERR_NULL     # a
+    assert f(A16 + 8, A16, A16, A16, None, A16, 16, 64, 64, None) == mx.MX_ERR_ALIGN
+    assert f(None, None, None, None, None, None, 0, 64, 64, None) == mx.MX_OK        # empty
+    assert f(A16, A16, A16, A16, None, A16, 65536, 64, 32768, None) == mx.MX_ERR_SHAPE
