@@ -22,7 +22,11 @@ the two large FP8 x FP8 configurations, each with its own roofline block.  `late
 small configurations (16x256x512, 1024^3 + bias and the three skinny A4W4 shapes): the same
 median, `graph_ms` (20 launches captured in one HIP graph, replayed; launch overhead amortized)
 and `cold_ms` (median of single launches, each after 512 MB were written to evict the caches).
-`act_quant` reports the standalone producer on [16384, 7168] against HBM bandwidth,
+Each of the three large GEMM blocks carries `vendor_bf16`: the vendor library's plain bf16 GEMM
+(torch.matmul) on the same shape, timed in alternation with ours (same clock and temperature),
+as context: what the bf16 MFMA reaches on this GPU without decodes or scales.  The next-layer
+leg times its fused and unfused variants in alternation too.  `act_quant` reports the standalone
+producer on [16384, 7168] against HBM bandwidth,
 `act_quant_fp4` the MXFP4 producer on the same input.  `cpu_baseline` times the oracle on a
 bounded sample of the same workload on the host.  Each roofline block names the kernel and grid
 of its dispatches and how many of them it timed (`trace`), so that a kernel trace of the same
@@ -69,14 +73,16 @@ ACT_QUANT_SOURCES = ["block_scaled_precision_act_amd/csrc/act_quant.hip",
 # act_quant_kernel<chunks per lane, output format, stochastic>: format 0 is E4M3, 4 packed E2M1
 AQ_E4M3_KERNEL = r"act_quant_kernel<\d+, 0, false>"
 AQ_E2M1_KERNEL = r"act_quant_kernel<\d+, 4, false>"
-# gemm_mx_kernel<A format, B format, bias, quantized output, epilogue, split-K> (256x256 tiles,
-# 256 threads) and gemm_bf16_kernel<same, BM, BN, WM, WN> (smaller tiles): format 0 is E4M3,
-# 4 packed E2M1
-GEMM_FP8_FP4_KERNEL = r"gemm_mx_kernel<0, 4, true, false, 0, false>"
-GEMM_FP8_FP4_QUANT_KERNEL = r"gemm_mx_kernel<0, 4, true, true, 0, false>"
+# gemm_mx_kernel<A format, B format, bias, quantized output, epilogue, split-K, tile width>
+# (256 x 256 or 256 x 224 tiles, 256 threads) and gemm_bf16_kernel<same first six, BM, BN, WM, WN>
+# (smaller tiles): format 0 is E4M3, 4 packed E2M1.  4096 x 7168 takes 256 x 224 tiles (512
+# tiles: two full waves of 256 CUs), the others 256 x 256.
+GEMM_FP8_FP4_KERNEL = r"gemm_mx_kernel<0, 4, true, false, 0, false, 224>"
+GEMM_FP8_FP4_QUANT_KERNEL = r"gemm_mx_kernel<0, 4, true, true, 0, false, 224>"
 GEMM_FP8_FP4_128_KERNEL = r"gemm_bf16_kernel<0, 4, true, false, 0, false, 128, 128,"
-GEMM_FP8_FP4_SPLITK_KERNEL = r"gemm_mx_kernel<0, 4, true, false, 0, true>"
-GEMM_FP8_FP8_KERNEL = r"gemm_mx_kernel<0, 0, false, false, 0, false>"
+GEMM_FP8_FP4_SPLITK_KERNEL = r"gemm_mx_kernel<0, 4, true, false, 0, true, 256>"
+GEMM_FP8_FP8_KERNEL = r"gemm_mx_kernel<0, 0, false, false, 0, false, 256>"
+C5_TILE_N = 224               # output tile width the library takes for 4096 x 7168
 # the kernels a default run times (the kernel-trace summary is of a default run); --all adds the
 # split-K comparison's two
 KERNEL_PATTERNS = (AQ_E4M3_KERNEL, AQ_E2M1_KERNEL, GEMM_FP8_FP4_KERNEL, GEMM_FP8_FP4_QUANT_KERNEL,
@@ -170,6 +176,60 @@ def timed(fn, torch):
     warm = settle(fn, torch)
     ms, _ = median_ms(fn, torch)
     return ms, warm, GROUPS * PER_GROUP
+
+
+def paired_ms(fns, torch):
+    """Median ms per call of each of `fns`, timed in alternation so that every one sees the same
+    clock and temperature (the clock of this GPU moves with its recent load): a settling phase
+    of at least SETTLE_MS that runs the functions in turn, then GROUPS rounds, each timing one
+    group of PER_GROUP back-to-back calls of every function, in turn, with HIP events on the
+    current stream."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for fn in fns:
+            for _ in range(PER_GROUP):
+                fn()
+        torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    per = [[] for _ in fns]
+    for _ in range(GROUPS):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        evs[0].record(st)
+        for i, fn in enumerate(fns):
+            for _ in range(PER_GROUP):
+                fn()
+            evs[i + 1].record(st)
+        torch.cuda.synchronize()
+        for i in range(len(fns)):
+            per[i].append(evs[i].elapsed_time(evs[i + 1]) / PER_GROUP)
+    return [statistics.median(x) for x in per]
+
+
+def vendor_pair(torch, ours, batch, M, N, K):
+    """The vendor library's plain bf16 GEMM (torch.matmul, which calls hipBLASLt) on the same
+    shape, timed in alternation with our launch `ours` (paired_ms): what the bf16 MFMA reaches on
+    this GPU with no decode and no scales, as context for the roofline fractions (not a path of
+    this library)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    lead = () if batch is None else (batch,)
+    a = torch.randn(lead + (M, K), device="cuda", dtype=torch.bfloat16, generator=g)
+    # the right operand already [K, N] and contiguous: no transposed view reaches bmm
+    b = torch.randn(lead + (K, N), device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(lead + (M, N), device="cuda", dtype=torch.bfloat16)
+
+    def mm():
+        torch.matmul(a, b, out=c)
+
+    ours_ms, vendor_ms = paired_ms([ours, mm], torch)
+    flops = 2.0 * M * N * K * (batch or 1)
+    del a, b, c
+    return {"vendor_ms": round(vendor_ms, 5),
+            "vendor_tflops": round(flops / (vendor_ms * 1e-3) / 1e12, 2),
+            "ours_ms": round(ours_ms, 5), "ours_over_vendor": round(vendor_ms / ours_ms, 4),
+            "note": "torch.matmul (hipBLASLt) on bf16 N(0,1) operands of the same shape, timed "
+                    "in alternation with this GEMM; ours_over_vendor = vendor time / our time"}
 
 
 def gemm_roofline(ms, flops, peak_kind, kernel_desc, pattern, grid, warm, n, profile_key=None,
@@ -321,14 +381,17 @@ def main():
     def gemm():
         mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
 
+    # the vendor comparison first, so that the leg's own timed launches are the last of the kernel
+    vendor = vendor_pair(torch, gemm, None, M, N, K)
     gemm_ms, warm, n = timed(gemm, torch)
-    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    tiles = ((M + 255) // 256) * ((N + C5_TILE_N - 1) // C5_TILE_N)
     out["roofline"] = gemm_roofline(
-        gemm_ms, flops, "fp8", "gemm_mx_kernel<fp8, fp4, bias> (E4M3/E2M1 decoded exactly to "
-        "bf16, bf16 MFMA)", GEMM_FP8_FP4_KERNEL, (tiles * GEMM_THREADS, 1), warm, n,
+        gemm_ms, flops, "fp8", "gemm_mx_kernel<fp8, fp4, bias> on 256x224 tiles (E4M3/E2M1 "
+        "decoded exactly to bf16, bf16 MFMA)", GEMM_FP8_FP4_KERNEL, (tiles * GEMM_THREADS, 1), warm, n,
         "gemm_fp8_fp4_4096x7168x2048")
     out["gemm_only_tflops"] = out["roofline"]["achieved"]
     progress(f"gemm 4096x7168x2048: {gemm_ms * 1e3:.2f} us")
+    out["roofline"]["vendor_bf16"] = vendor
     del x
 
     # ---- the two large FP8 x FP8 configurations (A quantized on the GPU by act_quant)
@@ -338,6 +401,7 @@ def main():
         mx, synth, torch, dev_u8, dev_bf16, stream, synth.fp8xfp8_batched_8x1024x2048x2048(),
         "gemm_fp8_fp8_batched_8x1024x2048x2048")
     progress("large fp8 x fp8 gemms done")
+
 
     # ---- the latency-bound configurations
     out["latency"] = bench_latency(mx, synth, torch, dev_u8, dev_bf16, stream, args.all)
@@ -378,8 +442,7 @@ def bench_next_layer(mx, torch, q, s, b, b_s, bias, c, stream, flops):
         mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
         mx.mx_act_quant(c, qn, qsn, stream=stream)
 
-    fused_ms, _, _ = timed(fused, torch)
-    unfused_ms, _, _ = timed(unfused, torch)
+    fused_ms, unfused_ms = paired_ms([fused, unfused], torch)
     return {"workload": "FP8xMXFP4 GEMM 4096x7168x2048 + bias -> E4M3 [4096, 7168] + "
                         "E8M0 [4096, 224] for the next layer",
             "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
@@ -427,6 +490,8 @@ def bench_large(mx, synth, torch, dev_u8, dev_bf16, stream, w, profile_key):
     def gemm():
         mx.mx_gemm_fp8_fp8(a, a_s, b, b_s, c, stream=stream)
 
+    # the vendor comparison first, so that the leg's own timed launches are the last of the kernel
+    vendor = vendor_pair(torch, gemm, w.batch, w.M, w.N, w.K)
     ms, warm, n = timed(gemm, torch)
     flops = 2.0 * w.M * w.N * w.K * batch
     tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
@@ -436,6 +501,7 @@ def bench_large(mx, synth, torch, dev_u8, dev_bf16, stream, w, profile_key):
     batch_txt = f"{w.batch} x " if w.batch else ""
     block["workload"] = (f"FP8xFP8 GEMM {batch_txt}{w.M}x{w.N}x{w.K}, 32x32 block-scaled E4M3 "
                          f"weights, activations through act_quant, no bias")
+    block["vendor_bf16"] = vendor
     del a, a_s, b, b_s, c
     return block
 

@@ -579,7 +579,7 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   if (g.workspace) {
     const SplitPlan plan = plan_split(g.M, g.N, g.K, g.batch);
     if (plan.splits > 1) {
-      if (mx_kernel_takes(g.K, plan.splits)) return launch_gemm_mx(AF, BF, g, &plan, stream);
+      if (mx_kernel_takes(g.K, plan.splits)) return launch_gemm_mx(AF, BF, g, &plan, 256, stream);
       return launch_split<AF, BF>(g, plan, dev.device, stream);
     }
   }
@@ -588,13 +588,17 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * g.batch;
   };
-  // A last partial wave of 256x256 tiles is not worth splitting further: on 4096x7168 (448 tiles,
-  // 1.75 waves) the 192 tiles of the second wave run 18% faster per CU than a full wave does, and
-  // finishing them as 256 tiles of 256x192 in a second launch measured the same total time.
   // Above half the CUs, one wave of 256x256 tiles beats the three or four waves of 128x128 tiles
   // the same output needs (a 128x128 step costs 0.37 of a 256x256 step for a quarter of the work).
+  // Where 256x224 tiles fill the last wave better, the large kernel takes those (mx_tile_n).  On
+  // 4096x7168 (448 tiles of 256x256: 1.75 waves of 256 CUs; 512 of 256x224: two full waves) that
+  // raises the CUs' busy share of the kernel's cycles from 0.76 to 0.86 but the time stays within
+  // 1%: with every CU busy the clock falls from 2.05 to 1.98 GHz (the chip is at its power limit
+  // under this load), as it does for a partial last wave's idle CUs in reverse (its tiles run
+  // faster per CU).
   if (2 * tiles(256, 256) > cus) {
-    if (mx_kernel_takes(g.K, 1)) return launch_gemm_mx(AF, BF, g, nullptr, stream);
+    if (mx_kernel_takes(g.K, 1))
+      return launch_gemm_mx(AF, BF, g, nullptr, mx_tile_n(g.M, g.N, g.batch, cus), stream);
     return launch_tile<AF, BF, 256, 256, 2, 4>(g, dev.device, stream);
   }
   if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, dev.device, stream);

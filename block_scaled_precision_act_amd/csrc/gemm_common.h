@@ -117,7 +117,8 @@ __device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_
 // returns); then the epilogue of one BM x BN tile from the accumulators of its WM x WN wavefronts:
 // fp32 + bias (+ residual, or GELU), one bf16 rounding, staged through LDS rows given by
 // tile_row(r) (BN * 2 bytes each, free for reuse: every wavefront is past its last operand read),
-// copied out with 16-byte stores; or, QUANT, the bf16 tile quantized per 32 columns.
+// copied out with 16-byte stores; or, QUANT, the bf16 values quantized per 32 columns straight
+// from the accumulators.
 // lds_bias holds the tile's BN bias values as fp32 when has_bias.
 template <int AF, bool QUANT, int EPI, bool SPLIT, int BM, int BN, int WM, int WN, class RowPtr>
 __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM / 32][BN / WN / 32],
@@ -207,17 +208,96 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
     part_lost = role != 1u;
   }
 
+  if constexpr (QUANT) {
+    // The quantized output, straight from the accumulators (no LDS staging).  Per 32-column
+    // block j of row 32 i + l32: lane (l32, h) holds the block's columns 8 r4 + 4 h + k
+    // (r4, k < 4), 16 of its 32 values, and lane l32 + 32 (h flipped) holds the other 16.  Each
+    // value is (sum + bias), GELU'd for EPI == kEpiGelu, rounded to bf16 once, exactly as the
+    // bf16 output would hold it; the block's largest |bf16| is the max of the two lanes' maxima
+    // (one exchange across the wavefront halves), and the codes are those act_quant gives for
+    // those bf16 values (the same arithmetic, mx_quant.h).  A second exchange hands each lane a
+    // contiguous half of the block's codes: 16 bytes (E4M3) or 8 (E2M1) per store; lane h = 0
+    // stores the block's E8M0 byte.  N % 32 == 0, so a block is inside the matrix or wholly
+    // outside it.
+    uint8_t* q = p.q + bz * p.stride_q;
+    uint8_t* qs = p.qs + bz * p.stride_qs;
+    const int nb = p.N / 32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int bcol = wn * WTN + 32 * j;                 // the block's first tile column
+      const int col0 = n0 + bcol;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = m0 + wm * WTM + 32 * i + l32;
+        const bool live = row < p.M && col0 < p.N;
+        uint32_t lo[4], hi[4];           // bf16 pairs of columns 8 r4 + 4 h + (0, 1) and (2, 3)
+        uint32_t amax = 0;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          v4f bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (has_bias) bias4 = *reinterpret_cast<const v4f*>(lds_bias + bcol + 8 * r4 + 4 * h);
+          float v[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[k] = acc[i][j][4 * r4 + k] + bias4[k];
+            if constexpr (EPI == kEpiGelu) v[k] = gelu_f32(v[k]);
+          }
+          lo[r4] = pk_bits(bf16x2{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1])});
+          hi[r4] = pk_bits(bf16x2{static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])});
+          amax = max(amax, abs_max_bits(uint4{lo[r4], hi[r4], 0u, 0u}));
+        }
+        amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 32)));
+        if constexpr (AF == kFp4) {
+          const uint32_t byte = fp4_scale_byte(amax);
+          const float sc = __uint_as_float(byte << 23);              // 2^E, a normal fp32
+          uint32_t c[4];                                              // 4 codes = 16 bits each
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) c[r4] = encode4_fp4(lo[r4], hi[r4], sc);
+          // h = 0 keeps columns 0-15 of the block (bytes 0-7), h = 1 columns 16-31 (bytes 8-15)
+          const uint32_t mine_lo = c[0] | (c[1] << 16), mine_hi = c[2] | (c[3] << 16);
+          const uint32_t got = static_cast<uint32_t>(
+              __shfl_xor(static_cast<int>(h ? mine_lo : mine_hi), 32));
+          const uint2 out = h ? uint2{(got & 0xFFFFu) | (c[2] << 16), (got >> 16) | (c[3] << 16)}
+                              : uint2{c[0] | (got << 16), c[1] | (got & 0xFFFF0000u)};
+          if (live) {
+            *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row) * (p.N / 2) + col0 / 2 + 8 * h) = out;
+            if (h == 0) qs[static_cast<int64_t>(row) * nb + (col0 >> 5)] = static_cast<uint8_t>(byte);
+          }
+        } else {
+          const uint32_t byte = act_scale_byte(amax);
+          const float inv_s = __uint_as_float((254u - byte) << 23);  // 2^-E, a normal fp32
+          uint32_t d[4];                                              // 4 codes each
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) d[r4] = encode4(lo[r4], hi[r4], inv_s);
+          // h = 0 keeps columns 0-15 (dwords of r4 = 0, 1 and the partner's), h = 1 columns 16-31
+          const uint32_t ga = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? d[0] : d[2]), 32));
+          const uint32_t gb = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? d[1] : d[3]), 32));
+          const uint4 out = h ? uint4{ga, d[2], gb, d[3]} : uint4{d[0], ga, d[1], gb};
+          if (live) {
+            *reinterpret_cast<uint4*>(q + static_cast<int64_t>(row) * p.N + col0 + 16 * h) = out;
+            if (h == 0) qs[static_cast<int64_t>(row) * nb + (col0 >> 5)] = static_cast<uint8_t>(byte);
+          }
+        }
+      }
+    }
+    return;
+  }
   // Epilogue, staged through LDS: fp32 + bias, one bf16 rounding, written into a row-major bf16
   // tile [BM][BN], then copied out in coalesced 16-byte row segments.  The MFMA takes B as its
   // first operand, so accumulator block (i, j) holds C^T: element 4 r4 + k of a lane is row
   // 32 i + l32 and column 32 j + 8 r4 + 4 h + k of the wavefront tile, four consecutive
   // columns of one row, written to LDS as one 8-byte store.  16-byte chunk c of tile row r sits
-  // at chunk c ^ tile_ch(r): the 16 rows that 16 lanes write in one pass land in 16 different
-  // 16-byte bank groups, and a row's chunks stay a permutation of themselves for the copy-out.
+  // at chunk tile_ch(r, c), c XOR a few bits of r: the 16 rows that 16 lanes write in one pass
+  // land in 16 different 16-byte bank groups (for 28-chunk rows, of 448 bytes, rows r and r + 1
+  // start 64 bytes of banks apart and the XOR of (r >> 2) & 3 does the rest), and a row's chunks
+  // stay a permutation of themselves for the copy-out.
   __syncthreads();                       // every wavefront is done reading the operand stages
   constexpr int kChunksPerRow = BN / 8;
+  static_assert(kChunksPerRow % 4 == 0, "tile width");
   auto tile_ch = [](int r, int c) {
-    return kChunksPerRow >= 16 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+    if constexpr (kChunksPerRow % 16 == 0) return c ^ (r & 15);
+    else if constexpr (kChunksPerRow % 8 == 0) return c ^ ((r >> 1) & 7);
+    else return c ^ ((r >> 2) & 3);
   };
   if constexpr (EPI == kEpiResidual) {
     // The residual tile is first copied into the LDS tile in the same layout, with coalesced
@@ -225,23 +305,25 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
     // outputs' places and overwrites them with the results.  The residual may be the output
     // itself: every read of the tile precedes the barrier before the copy-out.
     const uint16_t* res = p.res + bz * p.stride_res;
-    constexpr int kResStep = NT / kChunksPerRow;   // rows between a thread's chunks
-    constexpr int kResIters = BM / kResStep;
-    static_assert(NT % kChunksPerRow == 0 && BM % kResStep == 0, "residual rows");
+    constexpr int kResIters = BM * kChunksPerRow / NT;
+    static_assert((BM * kChunksPerRow) % NT == 0, "residual chunks");
     if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
         (reinterpret_cast<uintptr_t>(res) & 15u) == 0) {
-      // A tile inside a residual whose rows are 16-byte aligned: every thread loads its chunk
-      // column of all the tile's rows before storing any of it, so the loads are in flight
-      // together instead of one memory round trip per chunk.
-      const int trow0 = threadIdx.x / kChunksPerRow, tch = threadIdx.x % kChunksPerRow;
-      const uint16_t* src = res + static_cast<int64_t>(m0 + trow0) * p.N + n0 + tch * 8;
-      const int64_t step = static_cast<int64_t>(kResStep) * p.N;
+      // A tile inside a residual whose rows are 16-byte aligned: every thread loads all its
+      // chunks (chunk threadIdx + NT it of the tile, row-major) before storing any of them, so
+      // the loads are in flight together instead of one memory round trip per chunk.
       uint4 v[kResIters];
 #pragma unroll
-      for (int it = 0; it < kResIters; ++it) v[it] = *reinterpret_cast<const uint4*>(src + it * step);
+      for (int it = 0; it < kResIters; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+        v[it] = *reinterpret_cast<const uint4*>(res + static_cast<int64_t>(m0 + trow) * p.N + n0 +
+                                                tch * 8);
+      }
 #pragma unroll
       for (int it = 0; it < kResIters; ++it) {
-        const int trow = trow0 + it * kResStep;
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
         *reinterpret_cast<uint4*>(tile_row(trow) + tile_ch(trow, tch) * 16) = v[it];
       }
     } else {
@@ -309,58 +391,28 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
     }
   }
   __syncthreads();
-  if constexpr (QUANT) {
-    // Four consecutive lanes hold the four 16-byte chunks of one 32-column block of a row
-    // (kChunksPerRow % 4 == 0), and every lane of the workgroup runs every iteration (the tile's
-    // chunk count is a multiple of the workgroup size), so the quad permutes only mix live lanes.
-    // N % 32 == 0: a block is entirely inside or entirely outside the matrix.
-    static_assert(kChunksPerRow % 4 == 0 && (BM * kChunksPerRow) % NT == 0, "quad blocks");
-    uint8_t* q = p.q + bz * p.stride_q;
-    uint8_t* qs = p.qs + bz * p.stride_qs;
-    const int nb = p.N / 32;
-    // a fixed trip count, unrolled, so that several iterations' LDS reads are in flight together
-    constexpr int kQIters = BM * kChunksPerRow / NT;
-#pragma unroll 8
-    for (int it = 0; it < kQIters; ++it) {
-      const int idx = static_cast<int>(threadIdx.x) + it * NT;
-      const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-      const int row = m0 + trow, col = n0 + tch * 8;
-      const int ch = tile_ch(trow, tch);
-      const uint4 v = *reinterpret_cast<const uint4*>(tile_row(trow) + ch * 16);
-      if constexpr (AF == kFp4) {
-        const QuantChunkFp4 qc = quant_chunk_fp4(v);
-        if (row < p.M && col < p.N) {
-          *reinterpret_cast<uint32_t*>(q + static_cast<int64_t>(row) * (p.N / 2) + col / 2) = qc.codes;
-          if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
-        }
-      } else {
-        const QuantChunk qc = quant_chunk(v);
-        if (row < p.M && col < p.N) {
-          *reinterpret_cast<uint2*>(q + static_cast<int64_t>(row) * p.N + col) = qc.codes;
-          if ((tch & 3) == 0) qs[static_cast<int64_t>(row) * nb + (col >> 5)] = static_cast<uint8_t>(qc.byte);
-        }
-      }
-    }
-  } else {
+  {
     uint16_t* c = p.c + bz * p.stride_c;
-    // A tile wholly inside an output whose rows are 16-byte aligned: every thread copies the same
-    // chunk column of rows trow0 + kRowStep * it, all LDS reads issued before the stores.
-    constexpr int kRowStep = NT / kChunksPerRow;
-    constexpr int kIters = BM / kRowStep;
-    static_assert(NT % kChunksPerRow == 0 && BM % kRowStep == 0, "copy-out rows");
+    // A tile wholly inside an output whose rows are 16-byte aligned: thread t copies chunks
+    // t + NT it of the tile (row-major, so a wavefront's stores cover whole row segments), all LDS
+    // reads issued before the stores.
+    constexpr int kIters = BM * kChunksPerRow / NT;
+    static_assert((BM * kChunksPerRow) % NT == 0, "copy-out chunks");
     if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
         (reinterpret_cast<uintptr_t>(c) & 15u) == 0) {
-      const int trow0 = threadIdx.x / kChunksPerRow, tch = threadIdx.x % kChunksPerRow;
       uint4 v[kIters];
 #pragma unroll
       for (int it = 0; it < kIters; ++it) {
-        const int trow = trow0 + it * kRowStep;
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
         v[it] = *reinterpret_cast<const uint4*>(tile_row(trow) + tile_ch(trow, tch) * 16);
       }
-      uint16_t* dst = c + static_cast<int64_t>(m0 + trow0) * p.N + n0 + tch * 8;
-      const int64_t step = static_cast<int64_t>(kRowStep) * p.N;
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) *reinterpret_cast<uint4*>(dst + it * step) = v[it];
+      for (int it = 0; it < kIters; ++it) {
+        const int idx = static_cast<int>(threadIdx.x) + it * NT;
+        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+        *reinterpret_cast<uint4*>(c + static_cast<int64_t>(m0 + trow) * p.N + n0 + tch * 8) = v[it];
+      }
     } else {
       for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
         const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;

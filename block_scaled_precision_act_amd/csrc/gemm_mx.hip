@@ -50,6 +50,18 @@ constexpr int kStageBytes = 32768;         // A region (256 rows x 64 B), then B
 constexpr int kBRegion = 16384;
 constexpr uint32_t kOob = 0x80000000u;     // past any buffer bound
 
+// Wavefront grid and 32 x 32 blocks per wavefront of a 256 x BN output tile: 256 x 256 as 2 x 2
+// wavefronts of 128 x 128 (4 x 4 blocks); 256 x 224 as 4 x 1 wavefronts of 64 x 224 (2 x 7
+// blocks), for problems whose 256-wide tiles leave the last wave of workgroups part-empty.
+template <int BN>
+struct Shape {
+  static_assert(BN == 256 || BN == 224, "tile width");
+  static constexpr int kWM = BN == 256 ? 2 : 4;
+  static constexpr int kWN = kWaves / kWM;
+  static constexpr int kTM = kTile / kWM / 32;
+  static constexpr int kTN = BN / kWN / 32;
+};
+
 // Bytes of one operand row per K step (64 K).
 template <int FMT>
 constexpr int step_bytes() { return byte_codes(FMT) ? 64 : 32; }
@@ -69,8 +81,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // writes the 1 KB at stage offset (w * kPer + j) * 1024; its lane i fetches the 16 bytes that
 // belong at byte 16 i of that KB (row and physical unit from the offset, logical unit through
 // the swizzle).  The step's byte offset goes in the scalar offset, so a copy costs no vector
-// instruction; rows past the matrix read zeros through the buffer bound (their vector offset is
-// past it), and so does every lane of a step past the range (bit 31 set by `oob`).
+// instruction; rows past the matrix or past the tile's `rows_tile` read zeros through the buffer
+// bound (their vector offset is past it), and so does every lane of a step past the range (bit
+// 31 set by `oob`).
 template <int FMT>
 struct Copier {
   static constexpr int kRB = step_bytes<FMT>();
@@ -79,8 +92,8 @@ struct Copier {
   uint32_t voff[kPer];       // row * pitch + 16 u, or kOob
   uint32_t lds_off[kPer];    // stage-relative LDS byte offset of copy j (wavefront-uniform)
 
-  __device__ __forceinline__ void init(const uint8_t* base, int row0, int rows_valid, int K,
-                                       int wave, int lane, uint32_t region) {
+  __device__ __forceinline__ void init(const uint8_t* base, int row0, int rows_valid, int rows_tile,
+                                       int K, int wave, int lane, uint32_t region) {
     const uint32_t pitch = byte_codes(FMT) ? K : K / 2;
     rsrc = make_rsrc(base, static_cast<uint32_t>(rows_valid) * pitch);
 #pragma unroll
@@ -90,7 +103,7 @@ struct Copier {
       const int r = byte / kRB;
       const int u = ((byte % kRB) >> 4) ^ unit_swz<FMT>(r);
       const int row = row0 + r;
-      voff[j] = row < rows_valid ? static_cast<uint32_t>(row) * pitch + 16u * u : kOob;
+      voff[j] = r < rows_tile && row < rows_valid ? static_cast<uint32_t>(row) * pitch + 16u * u : kOob;
       lds_off[j] = region + static_cast<uint32_t>(chunk) * 1024u;
     }
   }
@@ -113,24 +126,24 @@ __device__ __forceinline__ void pin(bf16x8& v) {
   v = __builtin_bit_cast(bf16x8, u);
 }
 
-// One wavefront's view of one operand: 4 blocks of 32 rows (rows row_w + 32 i + l32).  Per K
+// One wavefront's view of one operand: NB blocks of 32 rows (rows row_w + 32 i + l32).  Per K
 // step the lane reads the raw codes of the 32-block h of its row: E4M3/E5M2 two 16-byte units
 // (u = 2h: sub-steps 0-1, kept in raw[0]; u = 2h + 1: sub-steps 2-3, raw[1]), E2M1 one (u = h,
 // all four sub-steps, in raw[step parity]).  Scale bytes come a group of 4 steps at a time: one
 // 8-byte load per block holds the group's 8 bytes of the lane's row (steps k..k+3, blocks h = 0
 // and 1 each), kept in one of two register sets by group parity.
-template <int FMT, bool BLOCK_SCALES>
+template <int FMT, bool BLOCK_SCALES, int NB>
 struct Frag {
   static constexpr int kRB = step_bytes<FMT>();
   static constexpr int kUnits = byte_codes(FMT) ? 2 : 1;
   uint32_t rd[kUnits];       // stage-relative LDS offset of block 0's unit q
-  uint4 raw[2][4];           // byte codes: unit 0 in raw[0]; E2M1: the unit, by step parity
-  uint4 raw1[2][4];          // byte codes: unit 1, by step parity
+  uint4 raw[2][NB];          // byte codes: unit 0 in raw[0]; E2M1: the unit, by step parity
+  uint4 raw1[2][NB];         // byte codes: unit 1, by step parity
   __amdgpu_buffer_rsrc_t srsrc;
-  uint32_t soff[4];          // byte offset of block i's scale row (or kOob)
-  uint2 sv[2][4];            // scale bytes of a group: parity, block
+  uint32_t soff[NB];         // byte offset of block i's scale row (or kOob)
+  uint2 sv[2][NB];           // scale bytes of a group: parity, block
   uint32_t hsh;              // 8 h: the lane's byte within a step's pair
-  float sc[4];               // scale values of the step being decoded
+  float sc[NB];              // scale values of the step being decoded
 
   __device__ __forceinline__ void init(const uint8_t* sbase, int row0, int rows_valid, int kb,
                                        int row_w, int l32, int h, uint32_t region) {
@@ -143,7 +156,7 @@ struct Frag {
     const int srows = BLOCK_SCALES ? (rows_valid + 31) / 32 : rows_valid;
     srsrc = make_rsrc(sbase, static_cast<uint32_t>(srows) * static_cast<uint32_t>(kb));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int row = row0 + row_w + 32 * i + l32;
       const int sr = BLOCK_SCALES ? row / 32 : row;
       soff[i] = sr < srows ? static_cast<uint32_t>(sr) * kb : kOob;
@@ -171,7 +184,7 @@ struct Frag {
   template <int GP, int SP>
   __device__ __forceinline__ void take_scales() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const uint32_t d = SP < 2 ? sv[GP][i].x : sv[GP][i].y;
       sc[i] = e8m0_value((d >> (16u * (SP & 1) + hsh)) & 0xFFu);
     }
@@ -194,8 +207,9 @@ struct Frag {
   }
 };
 
-template <int AF, int BF>
+template <int AF, int BF, int BN>
 struct Pipe {
+  static constexpr int TM = Shape<BN>::kTM, TN = Shape<BN>::kTN;
   static constexpr bool kBBlock = BF == kFp8;        // 32x32 block scales
   static constexpr int kCpA = Copier<AF>::kPer, kCpB = Copier<BF>::kPer;
   static constexpr int kCp = kCpA + kCpB;            // copies per wavefront and step
@@ -204,9 +218,9 @@ struct Pipe {
   static constexpr int cut(int q) { return q * kCp / 4; }
   Copier<AF> ca;
   Copier<BF> cb;
-  Frag<AF, false> fa;
-  Frag<BF, kBBlock> fb;
-  bf16x8 opa[2][4], opb[2][4];     // decoded operands, by sub-step parity
+  Frag<AF, false, TM> fa;
+  Frag<BF, kBBlock, TN> fb;
+  bf16x8 opa[2][TM], opb[2][TN];   // decoded operands, by sub-step parity
 
   template <int C>
   __device__ __forceinline__ void copy(uint8_t* stage, int kabs, uint32_t oob) {
@@ -228,13 +242,15 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 // Loads (vector memory), spread over the window between two barriers: in sub-steps 1-3 parts
 // 0-2 of the copies of step kl + 3, in sub-step 0 part 3 of the copies of step kl + 2; when kl
 // is the first step of a scale group, the next group's scale bytes in sub-step 2.
-// Tasks within a sub-step, in order, spread over the slots after its 16 MFMAs: raw reads, the
-// next step's scale values (sub-step 3), decodes of the next sub-step (sub-step 3: the next
+// Tasks within a sub-step, in order, spread over the slots after its TM x TN MFMAs: raw reads,
+// the next step's scale values (sub-step 3), decodes of the next sub-step (sub-step 3: the next
 // step's sub-step 0), copies, scale loads.
-template <int P8, int AF, int BF>
-__device__ __forceinline__ void mx_step(Pipe<AF, BF>& P, uint8_t* const (&st)[kStages],
-                                        v16f (&acc)[4][4], int k0, int kl, int k_end) {
-  using PP = Pipe<AF, BF>;
+template <int P8, int AF, int BF, int BN>
+__device__ __forceinline__ void mx_step(Pipe<AF, BF, BN>& P, uint8_t* const (&st)[kStages],
+                                        v16f (&acc)[Shape<BN>::kTM][Shape<BN>::kTN], int k0,
+                                        int kl, int k_end) {
+  using PP = Pipe<AF, BF, BN>;
+  constexpr int TM = PP::TM, TN = PP::TN, NM = TM * TN;
   constexpr int ST = P8 % kStages;
   constexpr int ST1 = (ST + 1) % kStages;
   constexpr int PAR = ST & 1, PAR1 = ST1 & 1;
@@ -251,14 +267,14 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF>& P, uint8_t* const (&st)[kS
     constexpr int ds = (s + 1) & 3;          // sub-step decoded (s == 3: the next step's 0)
     constexpr int dpar = s == 3 ? PAR1 : PAR;
     // raw reads of the next step: unit 0 (and the one E2M1 unit) in s = 1, unit 1 in s = 2
-    constexpr int kRdA = s == 1 || (s == 2 && kByteA) ? 4 : 0;
-    constexpr int kRdB = s == 1 || (s == 2 && kByteB) ? 4 : 0;
+    constexpr int kRdA = s == 1 || (s == 2 && kByteA) ? TM : 0;
+    constexpr int kRdB = s == 1 || (s == 2 && kByteB) ? TN : 0;
     constexpr int kScl = s == 3 ? 1 : 0;
-    constexpr int kDec = 8;
+    constexpr int kDec = TM + TN;
     constexpr int c0 = s == 0 ? PP::cut(3) : PP::cut(s - 1);
     constexpr int c1 = s == 0 ? PP::kCp : PP::cut(s);
     constexpr int kCpy = c1 - c0;
-    constexpr int kSld = (s == 2 && SP == 0) ? 8 : 0;
+    constexpr int kSld = (s == 2 && SP == 0) ? TM + TN : 0;
     constexpr int kTasks = kRdA + kRdB + kScl + kDec + kCpy + kSld;
     auto task = [&](auto tc) {
       constexpr int t = decltype(tc)::value;
@@ -270,13 +286,13 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF>& P, uint8_t* const (&st)[kS
         P.fa.template take_scales<N8 / 4, N8 % 4>();
         P.fb.template take_scales<N8 / 4, N8 % 4>();
       } else if constexpr (t < kRdA + kRdB + kScl + kDec) {
-        constexpr int d = t - kRdA - kRdB - kScl, i = d & 3;
-        if constexpr (d < 4) {
-          P.opa[nb][i] = P.fa.template decode<ds, i, dpar>();
-          pin(P.opa[nb][i]);
+        constexpr int d = t - kRdA - kRdB - kScl;
+        if constexpr (d < TM) {
+          P.opa[nb][d] = P.fa.template decode<ds, d, dpar>();
+          pin(P.opa[nb][d]);
         } else {
-          P.opb[nb][i] = P.fb.template decode<ds, i, dpar>();
-          pin(P.opb[nb][i]);
+          P.opb[nb][d - TM] = P.fb.template decode<ds, d - TM, dpar>();
+          pin(P.opb[nb][d - TM]);
         }
       } else if constexpr (t < kRdA + kRdB + kScl + kDec + kCpy) {
         constexpr int c = c0 + t - (kRdA + kRdB + kScl + kDec);
@@ -284,16 +300,16 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF>& P, uint8_t* const (&st)[kS
         else P.template copy<c>(st[(ST + 2) % kStages], kabs + 2, oob2);
       } else {
         constexpr int q = t - (kRdA + kRdB + kScl + kDec + kCpy);
-        if constexpr (q < 4) P.fa.template load_group<GP ^ 1, q>(kabs + 4, oobg);
-        else P.fb.template load_group<GP ^ 1, q - 4>(kabs + 4, oobg);
+        if constexpr (q < TM) P.fa.template load_group<GP ^ 1, q>(kabs + 4, oobg);
+        else P.fb.template load_group<GP ^ 1, q - TM>(kabs + 4, oobg);
       }
     };
-    static_for<0, 16>([&](auto mc) {
+    static_for<0, NM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int i = m >> 2, j = m & 3;
+      constexpr int i = m / TN, j = m % TN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P.opb[s & 1][j], P.opa[s & 1][i],
                                                           acc[i][j], 0, 0, 0);
-      static_for<m * kTasks / 16, (m + 1) * kTasks / 16>(task);
+      static_for<m * kTasks / NM, (m + 1) * kTasks / NM>(task);
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (s == 0) {
@@ -301,7 +317,7 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF>& P, uint8_t* const (&st)[kS
       // loads of the window since the previous barrier, i.e. the copies of step kl + 2 and the
       // scale group the previous step issued, if it did.  And every read of the stages the
       // copies of this window overwrite is done.
-      constexpr int kAfter = PP::kCp + ((P8 + 7) % 4 == 0 ? 8 : 0);
+      constexpr int kAfter = PP::kCp + ((P8 + 7) % 4 == 0 ? TM + TN : 0);
       static_assert(kAfter < 64, "vmcnt field");
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kAfter));
       __builtin_amdgcn_s_barrier();
@@ -311,8 +327,10 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF>& P, uint8_t* const (&st)[kS
   });
 }
 
-template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT>
+template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT, int BN>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
+  using SH = Shape<BN>;
+  static_assert(!SPLIT || BN == kTile, "the split handoff's partial tiles are 256 x 256");
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
@@ -323,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / SH::kWN, wn = wave % SH::kWN;
 
   int tile_id = blockIdx.x, ntiles = gridDim.x, split = 0;
   if constexpr (SPLIT) {
@@ -334,14 +352,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
   int tm, tn;
   tile_of(tile_id, ntiles, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t bz = blockIdx.y;
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int m0 = tm * kTile, n0 = tn * BN;
   const int kb = p.K / 32;
 
-  Pipe<AF, BF> P;
-  P.ca.init(p.a + bz * p.stride_a, m0, p.M, p.K, wave, lane, 0);
-  P.cb.init(p.b + bz * p.stride_b, n0, p.N, p.K, wave, lane, kBRegion);
-  P.fa.init(p.a_s + bz * p.stride_as, m0, p.M, kb, wm * 128, l32, h, 0);
-  P.fb.init(p.b_s + bz * p.stride_bs, n0, p.N, kb, wn * 128, l32, h, kBRegion);
+  Pipe<AF, BF, BN> P;
+  P.ca.init(p.a + bz * p.stride_a, m0, p.M, kTile, p.K, wave, lane, 0);
+  P.cb.init(p.b + bz * p.stride_b, n0, p.N, BN, p.K, wave, lane, kBRegion);
+  P.fa.init(p.a_s + bz * p.stride_as, m0, p.M, kb, wm * (kTile / SH::kWM), l32, h, 0);
+  P.fb.init(p.b_s + bz * p.stride_bs, n0, p.N, kb, wn * (BN / SH::kWN), l32, h, kBRegion);
 
   // The tile's bias as fp32 in LDS for the epilogue (thread c: column c).
   const bool has_bias = BIAS && (EPI == kEpiPlain || p.bias != nullptr);
@@ -358,19 +376,17 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
     KT = KT_all / p.splits;
   }
   const int k_end = k0 + KT;
-  v16f acc[4][4];
+  v16f acc[SH::kTM][SH::kTN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < SH::kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < SH::kTN; ++j) acc[i][j] = v16f{};
 
   // Prologue: scale group 0, the copies of steps 0 and 1 and parts 0-2 of step 2's (the loop's
   // step 0 issues part 3, and scale group 1).
-  using PP = Pipe<AF, BF>;
-  static_for<0, 4>([&](auto ic) {
-    P.fa.template load_group<0, decltype(ic)::value>(k0, 0u);
-    P.fb.template load_group<0, decltype(ic)::value>(k0, 0u);
-  });
+  using PP = Pipe<AF, BF, BN>;
+  static_for<0, SH::kTM>([&](auto ic) { P.fa.template load_group<0, decltype(ic)::value>(k0, 0u); });
+  static_for<0, SH::kTN>([&](auto ic) { P.fb.template load_group<0, decltype(ic)::value>(k0, 0u); });
   static_for<0, PP::kCp>([&](auto cc) { P.template copy<decltype(cc)::value>(st0, k0, 0u); });
   static_for<0, PP::kCp>([&](auto cc) {
     P.template copy<decltype(cc)::value>(st1, k0 + 1, past(k0 + 1, k_end));
@@ -382,25 +398,31 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PP::kCp + PP::cut(3)));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  static_for<0, 4>([&](auto ic) {
+  static_for<0, SH::kTM>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     P.fa.template read<0, i, 0>(st0);
-    P.fb.template read<0, i, 0>(st0);
     if constexpr (byte_codes(AF)) P.fa.template read<1, i, 0>(st0);
-    if constexpr (byte_codes(BF)) P.fb.template read<1, i, 0>(st0);
+  });
+  static_for<0, SH::kTN>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    P.fb.template read<0, j, 0>(st0);
+    if constexpr (byte_codes(BF)) P.fb.template read<1, j, 0>(st0);
   });
   P.fa.template take_scales<0, 0>();
   P.fb.template take_scales<0, 0>();
-  static_for<0, 4>([&](auto ic) {
+  static_for<0, SH::kTM>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     P.opa[0][i] = P.fa.template decode<0, i, 0>();
-    P.opb[0][i] = P.fb.template decode<0, i, 0>();
+  });
+  static_for<0, SH::kTN>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    P.opb[0][j] = P.fb.template decode<0, j, 0>();
   });
 
   for (int kl = 0; kl < KT; kl += 8) {
     static_for<0, 8>([&](auto pc) {
       constexpr int p8 = decltype(pc)::value;
-      mx_step<p8>(P, st, acc, k0, kl + p8, k_end);
+      mx_step<p8, AF, BF, BN>(P, st, acc, k0, kl + p8, k_end);
     });
   }
   // The copies issued for steps past the range may still be landing in the stages the
@@ -409,57 +431,71 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
 
   auto tile_row = [&](int r) -> uint8_t* {
     uint8_t* const base = r < 64 ? st0 : r < 128 ? st1 : r < 192 ? st2 : st3;
-    return base + (r & 63) * (kTile * 2);
+    return base + (r & 63) * (BN * 2);
   };
-  finish_tile<AF, QUANT, EPI, SPLIT, kTile, kTile, 2, 2>(p, acc, tile_row, lds_bias, has_bias,
-                                                         split, tile_id, m0, n0, bz);
+  finish_tile<AF, QUANT, EPI, SPLIT, kTile, BN, SH::kWM, SH::kWN>(p, acc, tile_row, lds_bias,
+                                                                  has_bias, split, tile_id, m0,
+                                                                  n0, bz);
 }
 
-template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT>
+template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT, int BN = kTile>
 hipError_t launch_mx(const Args& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_mx_kernel<AF, BF, BIAS, QUANT, EPI, SPLIT>), grid, dim3(kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((gemm_mx_kernel<AF, BF, BIAS, QUANT, EPI, SPLIT, BN>), grid, dim3(kThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 
-template <int AF, int BF>
-hipError_t launch_formats_mx(const GemmProblem& g, const SplitPlan* plan, hipStream_t stream) {
+template <int AF, int BF, int BN>
+hipError_t launch_tiles_mx(const GemmProblem& g, const SplitPlan* plan, hipStream_t stream) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
-         (g.M + kTile - 1) / kTile, (g.N + kTile - 1) / kTile,
+         (g.M + kTile - 1) / kTile, (g.N + BN - 1) / BN,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
          g.q, g.qs, g.stride_q, g.stride_qs, g.residual, g.stride_res,
          nullptr, nullptr, 1};
-  if (plan) {
-    uint8_t* ws = static_cast<uint8_t*>(g.workspace);
-    p.ws = reinterpret_cast<float*>(ws + plan->counter_bytes);
-    p.counters = reinterpret_cast<uint32_t*>(ws);
-    p.splits = plan->splits;
-    dim3 grid(p.tiles_m * p.tiles_n * plan->splits, 1);
-    return g.bias ? launch_mx<AF, BF, true, false, kEpiPlain, true>(p, grid, stream)
-                  : launch_mx<AF, BF, false, false, kEpiPlain, true>(p, grid, stream);
+  if constexpr (BN == kTile) {
+    if (plan) {
+      uint8_t* ws = static_cast<uint8_t*>(g.workspace);
+      p.ws = reinterpret_cast<float*>(ws + plan->counter_bytes);
+      p.counters = reinterpret_cast<uint32_t*>(ws);
+      p.splits = plan->splits;
+      dim3 grid(p.tiles_m * p.tiles_n * plan->splits, 1);
+      return g.bias ? launch_mx<AF, BF, true, false, kEpiPlain, true>(p, grid, stream)
+                    : launch_mx<AF, BF, false, false, kEpiPlain, true>(p, grid, stream);
+    }
   }
   dim3 grid(p.tiles_m * p.tiles_n, g.batch);
   if constexpr (AF == kFp8 || AF == kFp4) {
     if (g.q) {
-      if (g.epi == kEpiGelu) return launch_mx<AF, BF, true, true, kEpiGelu, false>(p, grid, stream);
-      return g.bias ? launch_mx<AF, BF, true, true, kEpiPlain, false>(p, grid, stream)
-                    : launch_mx<AF, BF, false, true, kEpiPlain, false>(p, grid, stream);
+      if (g.epi == kEpiGelu)
+        return launch_mx<AF, BF, true, true, kEpiGelu, false, BN>(p, grid, stream);
+      return g.bias ? launch_mx<AF, BF, true, true, kEpiPlain, false, BN>(p, grid, stream)
+                    : launch_mx<AF, BF, false, true, kEpiPlain, false, BN>(p, grid, stream);
     }
   }
-  if (g.epi == kEpiResidual) return launch_mx<AF, BF, true, false, kEpiResidual, false>(p, grid, stream);
-  if (g.epi == kEpiGelu) return launch_mx<AF, BF, true, false, kEpiGelu, false>(p, grid, stream);
-  return g.bias ? launch_mx<AF, BF, true, false, kEpiPlain, false>(p, grid, stream)
-                : launch_mx<AF, BF, false, false, kEpiPlain, false>(p, grid, stream);
+  if (g.epi == kEpiResidual)
+    return launch_mx<AF, BF, true, false, kEpiResidual, false, BN>(p, grid, stream);
+  if (g.epi == kEpiGelu) return launch_mx<AF, BF, true, false, kEpiGelu, false, BN>(p, grid, stream);
+  return g.bias ? launch_mx<AF, BF, true, false, kEpiPlain, false, BN>(p, grid, stream)
+                : launch_mx<AF, BF, false, false, kEpiPlain, false, BN>(p, grid, stream);
+}
+
+template <int AF, int BF>
+hipError_t launch_formats_mx(const GemmProblem& g, const SplitPlan* plan, int tile_n,
+                             hipStream_t stream) {
+  if (tile_n == 224 && !plan) return launch_tiles_mx<AF, BF, 224>(g, nullptr, stream);
+  return launch_tiles_mx<AF, BF, kTile>(g, plan, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mx(int a_fmt, int b_fmt, const GemmProblem& p, const SplitPlan* plan,
-                          hipStream_t stream) {
-  if (a_fmt == kFp8 && b_fmt == kFp4) return launch_formats_mx<kFp8, kFp4>(p, plan, stream);
-  if (a_fmt == kFp8 && b_fmt == kFp8) return launch_formats_mx<kFp8, kFp8>(p, plan, stream);
-  if (a_fmt == kFp4 && b_fmt == kFp4) return launch_formats_mx<kFp4, kFp4>(p, plan, stream);
-  if (a_fmt == kBf8 && b_fmt == kFp8Rows) return launch_formats_mx<kBf8, kFp8Rows>(p, plan, stream);
+                          int tile_n, hipStream_t stream) {
+  if (tile_n != kTile && tile_n != 224) return hipErrorInvalidValue;
+  if (a_fmt == kFp8 && b_fmt == kFp4) return launch_formats_mx<kFp8, kFp4>(p, plan, tile_n, stream);
+  if (a_fmt == kFp8 && b_fmt == kFp8) return launch_formats_mx<kFp8, kFp8>(p, plan, tile_n, stream);
+  if (a_fmt == kFp4 && b_fmt == kFp4) return launch_formats_mx<kFp4, kFp4>(p, plan, tile_n, stream);
+  if (a_fmt == kBf8 && b_fmt == kFp8Rows)
+    return launch_formats_mx<kBf8, kFp8Rows>(p, plan, tile_n, stream);
   return hipErrorInvalidValue;
 }
 

@@ -101,15 +101,29 @@ hipError_t launch_quant_transpose(const uint16_t* x, uint8_t* q, uint8_t* s, int
 // FP8-operand kinds: exact bf16 decode + bf16 MFMA (gemm_bf16.hip).
 hipError_t launch_gemm_bf16(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
                             hipStream_t stream);
-// The same GEMMs on 256x256 tiles with one wavefront per SIMD and operands staged raw into LDS
-// by direct-to-LDS loads (gemm_mx.hip); `plan` non-null: split-K with p.workspace.  It runs K in
-// loop iterations of 8 steps of 64 (and reads scale bytes 4 steps at a time with 8-byte loads),
-// so it takes K % 512 == 0, and for a split, ranges of a multiple of 8 steps.
+// The same GEMMs on 256 x tile_n tiles (tile_n 256 or 224) with one wavefront per SIMD and
+// operands staged raw into LDS by direct-to-LDS loads (gemm_mx.hip); `plan` non-null: split-K
+// with p.workspace (256 x 256 tiles only).  It runs K in loop iterations of 8 steps of 64 (and
+// reads scale bytes 4 steps at a time with 8-byte loads), so it takes K % 512 == 0, and for a
+// split, ranges of a multiple of 8 steps.
 inline bool mx_kernel_takes(int64_t K, int splits) {
   return K > 0 && K % 512 == 0 && ((K / 64) % (8 * splits)) == 0;
 }
 hipError_t launch_gemm_mx(int a_fmt, int b_fmt, const GemmProblem& p, const SplitPlan* plan,
-                          hipStream_t stream);
+                          int tile_n, hipStream_t stream);
+
+// Output tile width for that kernel: 224 where the problem's tiles of 256 x 224 fill the CUs'
+// waves enough better than 256 x 256 tiles do to finish sooner, counting a wave of the narrower
+// tiles as 224/256 of a wave of the wider (e.g. 4096 x 7168: 448 tiles of 256 x 256 take two
+// waves of 256 CUs with the second one 3/4 full; 512 tiles of 256 x 224 take two full waves of
+// 7/8 the work each); 256 otherwise.
+inline int mx_tile_n(int64_t M, int64_t N, int64_t batch, int64_t cus) {
+  auto waves = [&](int64_t bn) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + bn - 1) / bn) * batch;
+    return (tiles + cus - 1) / cus;
+  };
+  return waves(224) * 224 < waves(256) * 256 ? 224 : 256;
+}
 // Both operands MXFP4 on the scaled f8f6f4 MFMA (gemm_fp4.hip).
 hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream);
 

@@ -89,22 +89,28 @@ struct QuantChunkFp4 {
   uint32_t byte;    // E8M0 byte of the 32-block
 };
 
-__device__ __forceinline__ QuantChunkFp4 quant_chunk_fp4(uint4 w) {
-  const uint32_t amax_bits = quad_max(abs_max_bits(w));
+// E8M0 byte of a 32-block for MXFP4 from the largest |bf16| pattern of the block.
+__device__ __forceinline__ uint32_t fp4_scale_byte(uint32_t amax_bits) {
   const uint32_t ab = __float_as_uint(fmaxf(__uint_as_float(amax_bits << 16), 1e-4f));
-  QuantChunkFp4 r;
-  r.byte = ((ab >> 23) & 0xFFu) - 2u + ((ab & 0x7FFFFFu) > 0x400000u);
-  const float s = __uint_as_float(r.byte << 23);                 // 2^E, a normal fp32
+  return ((ab >> 23) & 0xFFu) - 2u + ((ab & 0x7FFFFFu) > 0x400000u);
+}
+
+// Four bf16 (two packed pairs) divided by s = 2^E -> four E2M1 codes in the low 16 bits
+// (element 0 in the low nibble).
+__device__ __forceinline__ uint32_t encode4_fp4(uint32_t lo_pair, uint32_t hi_pair, float s) {
   uint32_t c = 0;
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.x << 16),
-                                               __uint_as_float(w.x & 0xFFFF0000u), s, 0);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.y << 16),
-                                               __uint_as_float(w.y & 0xFFFF0000u), s, 1);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.z << 16),
-                                               __uint_as_float(w.z & 0xFFFF0000u), s, 2);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(w.w << 16),
-                                               __uint_as_float(w.w & 0xFFFF0000u), s, 3);
-  r.codes = c;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(lo_pair << 16),
+                                               __uint_as_float(lo_pair & 0xFFFF0000u), s, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float(hi_pair << 16),
+                                               __uint_as_float(hi_pair & 0xFFFF0000u), s, 1);
+  return c;
+}
+
+__device__ __forceinline__ QuantChunkFp4 quant_chunk_fp4(uint4 w) {
+  QuantChunkFp4 r;
+  r.byte = fp4_scale_byte(quad_max(abs_max_bits(w)));
+  const float s = __uint_as_float(r.byte << 23);                 // 2^E, a normal fp32
+  r.codes = encode4_fp4(w.x, w.y, s) | (encode4_fp4(w.z, w.w, s) << 16);
   return r;
 }
 

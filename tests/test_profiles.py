@@ -60,7 +60,7 @@ def test_summarize_busy_arithmetic(tmp_path):
     busy.mkdir()
     _write_csv(busy / "run_agent_info.csv", ["Name", "Simd_Count", "Cu_Count", "Num_Xcc"],
                [["gfx950", 1024, 256, 8]])
-    gemm = ("void mx::(anonymous namespace)::gemm_mx_kernel<0, 4, true, false, 0, false>"
+    gemm = ("void mx::(anonymous namespace)::gemm_mx_kernel<0, 4, true, false, 0, false, 224>"
             "(mx::(anonymous namespace)::Args)")
     _write_csv(busy / "run_kernel_trace.csv", ["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
                                                 "End_Timestamp"],
