@@ -113,6 +113,23 @@ __device__ __forceinline__ void tile_of(int bid, int nb, int tiles_m, int tiles_
   tn = in_g / gsize;
 }
 
+// Tile coordinates of split tile `t` (workgroups 2 t and 2 t + 1 take its two K ranges).
+// Workgroups are dealt to the 8 XCDs in turn (workgroup b to XCD b % 8), so XCD x runs range
+// x % 2 of the tiles t = 4 j + x / 2.  With two ranges and a tile count divisible by 4, tile t is
+// renumbered so that XCDs 2 q and 2 q + 1 hold the q-th quarter of the tiles in row-major order:
+// a band of whole tile rows, whose A panels (the larger operand of a down-projection) then come
+// through one XCD's L2 for each range instead of four.  Otherwise the plain tile map.
+__device__ __forceinline__ void split_tile_of(int t, int nt, int splits, int tiles_m, int tiles_n,
+                                              int& tm, int& tn) {
+  if (splits == 2 && (nt & 3) == 0) {
+    const int r = (t & 3) * (nt >> 2) + (t >> 2);
+    tm = r / tiles_n;
+    tn = r % tiles_n;
+  } else {
+    tile_of(t, nt, tiles_m, tiles_n, tm, tn);
+  }
+}
+
 // After the main loop: for SPLIT, the partial-tile handoff (a workgroup whose range arrived first
 // returns); then the epilogue of one BM x BN tile from the accumulators of its WM x WN wavefronts:
 // fp32 + bias (+ residual, or GELU), one bf16 rounding, staged through LDS rows given by

@@ -344,13 +344,15 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
   const int wm = wave / SH::kWN, wn = wave % SH::kWN;
 
   int tile_id = blockIdx.x, ntiles = gridDim.x, split = 0;
+  int tm, tn;
   if constexpr (SPLIT) {
     split = blockIdx.x % p.splits;
     tile_id = blockIdx.x / p.splits;
     ntiles = gridDim.x / p.splits;
+    split_tile_of(tile_id, ntiles, p.splits, p.tiles_m, p.tiles_n, tm, tn);
+  } else {
+    tile_of(tile_id, ntiles, p.tiles_m, p.tiles_n, tm, tn);
   }
-  int tm, tn;
-  tile_of(tile_id, ntiles, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t bz = blockIdx.y;
   const int m0 = tm * kTile, n0 = tn * BN;
   const int kb = p.K / 32;
