@@ -329,3 +329,24 @@ def test_splitk_noalloc_argument_errors(lib):
     assert f(A16 + 8, A16, A16, A16, None, A16, 16, 64, 64, None) == mx.MX_ERR_ALIGN
     assert f(None, None, None, None, None, None, 0, 64, 64, None) == mx.MX_OK        # empty
     assert f(A16, A16, A16, A16, None, A16, 65536, 64, 32768, None) == mx.MX_ERR_SHAPE
+
+
+def test_c_driver_links_and_reports_missing_device(tmp_path):
+    # The C program that drives the ABI from C (tests/c_abi) is built and links against the
+    # library and the HIP runtime; without a GPU it reports that and exits with status 1.
+    import importlib.util
+    import shutil
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("mx_c_driver_build",
+                                                  os.path.join(here, "c_abi", "build.py"))
+    c_build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(c_build)
+    exe = c_build.build()
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the GPU test runs the program")
+    (tmp_path / "cases.txt").write_text("")
+    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "no gfx950 device" in r.stderr
+    assert shutil.which("gcc") or shutil.which("cc")

@@ -138,3 +138,13 @@ def test_fp4_output_rejects_ragged_n(mx, M):
     with pytest.raises(mx.MxError) as e:
         mx.mx_gemm_fp4_fp4_quant(dev_u8(w.a), dev_u8(w.a_s), dev_u8(w.b), dev_u8(w.b_s), q, qs)
     assert e.value.status == mx.MX_ERR_SHAPE
+
+
+# The large-problem kernel (256 x 256 or 256 x 224 tiles) quantizes straight from its
+# accumulators: MXFP4 output from an FP4 A operand, and the E4M3 output after GELU.
+@pytest.mark.parametrize("a_kind,M,N,K", [("fp4", 2048, 7168, 512), ("fp4", 4096, 4096, 1024),
+                                          ("acts", 2048, 7168, 512), ("acts", 4000, 4096, 512)])
+@pytest.mark.parametrize("gelu", [False, True])
+def test_large_kernel_quantized_outputs(mx, a_kind, M, N, K, gelu):
+    w = synth.gemm_inputs(a_kind, "fp4", M, N, K, seed=M + N + K + gelu, with_bias=True)
+    check(mx, w, gelu)
