@@ -130,17 +130,31 @@ __device__ __forceinline__ void split_tile_of(int t, int nt, int splits, int til
   }
 }
 
+// Place of 16-byte chunk c of row r in the epilogue's bf16 LDS tile of CPR chunks a row: c XOR
+// a few bits of r (rows 16 apart share the pattern).  The XOR is its own inverse, so the same
+// function maps a stored place back to the chunk it holds.
+template <int CPR>
+__device__ __forceinline__ int tile_chunk(int r, int c) {
+  static_assert(CPR % 4 == 0, "tile width");
+  if constexpr (CPR % 16 == 0) return c ^ (r & 15);
+  else if constexpr (CPR % 8 == 0) return c ^ ((r >> 1) & 7);
+  else return c ^ ((r >> 2) & 3);
+}
+
 // After the main loop: for SPLIT, the partial-tile handoff (a workgroup whose range arrived first
 // returns); then the epilogue of one BM x BN tile from the accumulators of its WM x WN wavefronts:
 // fp32 + bias (+ residual, or GELU), one bf16 rounding, staged through LDS rows given by
 // tile_row(r) (BN * 2 bytes each, free for reuse: every wavefront is past its last operand read),
 // copied out with 16-byte stores; or, QUANT, the bf16 values quantized per 32 columns straight
 // from the accumulators.
-// lds_bias holds the tile's BN bias values as fp32 when has_bias.
+// lds_bias holds the tile's BN bias values as fp32 when has_bias.  res_in_lds (residual epilogue):
+// the main loop has already copied the residual tile into the LDS tile, in its layout, and every
+// wavefront has waited for its own copies; the barrier below makes them visible.
 template <int AF, bool QUANT, int EPI, bool SPLIT, int BM, int BN, int WM, int WN, class RowPtr>
 __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM / 32][BN / WN / 32],
                                             RowPtr tile_row, const float* lds_bias, bool has_bias,
-                                            int split, int tile_id, int m0, int n0, int64_t bz) {
+                                            int split, int tile_id, int m0, int n0, int64_t bz,
+                                            bool res_in_lds = false) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -311,11 +325,7 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
   __syncthreads();                       // every wavefront is done reading the operand stages
   constexpr int kChunksPerRow = BN / 8;
   static_assert(kChunksPerRow % 4 == 0, "tile width");
-  auto tile_ch = [](int r, int c) {
-    if constexpr (kChunksPerRow % 16 == 0) return c ^ (r & 15);
-    else if constexpr (kChunksPerRow % 8 == 0) return c ^ ((r >> 1) & 7);
-    else return c ^ ((r >> 2) & 3);
-  };
+  auto tile_ch = [](int r, int c) { return tile_chunk<kChunksPerRow>(r, c); };
   if constexpr (EPI == kEpiResidual) {
     // The residual tile is first copied into the LDS tile in the same layout, with coalesced
     // 16-byte loads (zeros outside the matrix); each thread below reads the residual at its own
@@ -324,47 +334,49 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
     const uint16_t* res = p.res + bz * p.stride_res;
     constexpr int kResIters = BM * kChunksPerRow / NT;
     static_assert((BM * kChunksPerRow) % NT == 0, "residual chunks");
-    if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
-        (reinterpret_cast<uintptr_t>(res) & 15u) == 0) {
-      // A tile inside a residual whose rows are 16-byte aligned: every thread loads all its
-      // chunks (chunk threadIdx + NT it of the tile, row-major) before storing any of them, so
-      // the loads are in flight together instead of one memory round trip per chunk.
-      uint4 v[kResIters];
+    if (!res_in_lds) {
+      if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
+          (reinterpret_cast<uintptr_t>(res) & 15u) == 0) {
+        // A tile inside a residual whose rows are 16-byte aligned: every thread loads all its
+        // chunks (chunk threadIdx + NT it of the tile, row-major) before storing any of them, so
+        // the loads are in flight together instead of one memory round trip per chunk.
+        uint4 v[kResIters];
 #pragma unroll
-      for (int it = 0; it < kResIters; ++it) {
-        const int idx = static_cast<int>(threadIdx.x) + it * NT;
-        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-        v[it] = *reinterpret_cast<const uint4*>(res + static_cast<int64_t>(m0 + trow) * p.N + n0 +
-                                                tch * 8);
-      }
-#pragma unroll
-      for (int it = 0; it < kResIters; ++it) {
-        const int idx = static_cast<int>(threadIdx.x) + it * NT;
-        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-        *reinterpret_cast<uint4*>(tile_row(trow) + tile_ch(trow, tch) * 16) = v[it];
-      }
-    } else {
-      for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
-        const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-        const int row = m0 + trow, col = n0 + tch * 8;
-        const int ch = tile_ch(trow, tch);
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (row < p.M && col < p.N) {
-          const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
-          if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-            v = *reinterpret_cast<const uint4*>(src);
-          } else {
-            uint32_t e[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) e[k] = col + k < p.N ? src[k] : 0u;
-            v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                      e[6] | (e[7] << 16)};
-          }
+        for (int it = 0; it < kResIters; ++it) {
+          const int idx = static_cast<int>(threadIdx.x) + it * NT;
+          const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+          v[it] = *reinterpret_cast<const uint4*>(res + static_cast<int64_t>(m0 + trow) * p.N + n0 +
+                                                  tch * 8);
         }
-        *reinterpret_cast<uint4*>(tile_row(trow) + ch * 16) = v;
+#pragma unroll
+        for (int it = 0; it < kResIters; ++it) {
+          const int idx = static_cast<int>(threadIdx.x) + it * NT;
+          const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+          *reinterpret_cast<uint4*>(tile_row(trow) + tile_ch(trow, tch) * 16) = v[it];
+        }
+      } else {
+        for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {
+          const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
+          const int row = m0 + trow, col = n0 + tch * 8;
+          const int ch = tile_ch(trow, tch);
+          uint4 v = {0u, 0u, 0u, 0u};
+          if (row < p.M && col < p.N) {
+            const uint16_t* src = res + static_cast<int64_t>(row) * p.N + col;
+            if (col + 8 <= p.N && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+              v = *reinterpret_cast<const uint4*>(src);
+            } else {
+              uint32_t e[8];
+#pragma unroll
+              for (int k = 0; k < 8; ++k) e[k] = col + k < p.N ? src[k] : 0u;
+              v = uint4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                        e[6] | (e[7] << 16)};
+            }
+          }
+          *reinterpret_cast<uint4*>(tile_row(trow) + ch * 16) = v;
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {

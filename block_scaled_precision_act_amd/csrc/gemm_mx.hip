@@ -229,6 +229,62 @@ struct Pipe {
   }
 };
 
+// Residual epilogue: the bf16 residual tile, copied global -> LDS during the last K steps into the
+// operand stages as they fall free, already in the epilogue's tile layout (rows 64 s .. 64 s + 63
+// in stage s, tile_chunk swizzle), so the epilogue reads it from LDS without a memory round trip
+// of its own.  Each 64-row slice is kPer 1 KB copies per wavefront; lane i of copy j brings the
+// 16-byte chunk stored at byte 16 i of the slice's KB number (wave * kPer + j).  The copies take
+// the slots of the operand copies that steps past the range would issue (one load each, so every
+// wait count of the loop is unchanged; a slot beyond kPer loads zeros into the stage's spare
+// bytes), and the rest leave after the last step's barrier.  Only a tile inside the matrix with
+// 16-byte aligned rows (`on`) reads its residual this way; for any other tile the buffer holds no
+// bytes, so the same copies load zeros (no branch: the compiler's wait counting keeps telling
+// the stages apart) and the epilogue loads the residual itself.
+template <int BN>
+struct ResTail {
+  static constexpr int kChunks = BN / 8;                 // 16-byte chunks a tile row
+  static constexpr int kSliceBytes = 64 * BN * 2;
+  static constexpr int kPer = kSliceBytes / 1024 / kWaves;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t slice_bytes;      // 64 rows of the residual
+  uint32_t pitch;            // N, in elements
+  int wave, lane;
+  bool on;
+
+  __device__ __forceinline__ void init(const Args& p, int m0, int n0, int64_t bz, int wave_,
+                                       int lane_) {
+    const uint16_t* res = p.res + bz * p.stride_res;
+    wave = wave_;
+    lane = lane_;
+    on = m0 + kTile <= p.M && n0 + BN <= p.N && (p.N & 7) == 0 &&
+         (reinterpret_cast<uintptr_t>(res) & 15u) == 0 && p.N <= (1 << 22);
+    pitch = static_cast<uint32_t>(p.N);
+    slice_bytes = 128u * pitch;
+    rsrc = make_rsrc(on ? res + static_cast<int64_t>(m0) * p.N + n0 : res,
+                     on ? (255u * pitch + BN) * 2u : 0u);
+  }
+
+  // Copy J of slice `slice` into `stage`; J >= kPer: zeros into the stage's spare bytes.
+  template <int J, int kCp>
+  __device__ __forceinline__ void issue(uint8_t* stage, int slice) const {
+    if constexpr (J < kPer) {
+      const int q = (wave * kPer + J) * 64 + lane;          // stored chunk within the slice
+      const int r = q / kChunks;
+      const int c = tile_chunk<kChunks>(r, q % kChunks);    // the chunk it holds
+      const uint32_t voff = (static_cast<uint32_t>(r) * pitch + 8u * c) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_ptr_t)(stage + (wave * kPer + J) * 1024), 16, static_cast<int>(voff),
+          static_cast<int>(slice * slice_bytes), 0, 0);
+    } else {
+      constexpr int kFill = kCp - kPer;
+      static_assert(kSliceBytes + kWaves * kFill * 1024 <= kStageBytes, "stage spare bytes");
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_ptr_t)(stage + kSliceBytes + (wave * kFill + (J - kPer)) * 1024), 16,
+          static_cast<int>(kOob), 0, 0, 0);
+    }
+  }
+};
+
 // s_waitcnt operand: vmcnt(n) lgkmcnt(0), expcnt at its maximum (gfx9 encoding).
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
@@ -245,11 +301,25 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 // Tasks within a sub-step, in order, spread over the slots after its TM x TN MFMAs: raw reads,
 // the next step's scale values (sub-step 3), decodes of the next sub-step (sub-step 3: the next
 // step's sub-step 0), copies, scale loads.
-template <int P8, int AF, int BF, int BN>
-__device__ __forceinline__ void mx_step(Pipe<AF, BF, BN>& P, uint8_t* const (&st)[kStages],
+// TAIL: the range's last 8 steps in a kernel with the residual epilogue.  The copy slots of
+// steps past the range bring the residual tile (ResTail); the scale group past the range is not
+// loaded (its registers would be dead, and the compiler, reusing them, would wait for the loads);
+// the last step reads and decodes nothing for the step after it, and after its barrier the
+// residual copies with no slot leave: those of slice 2 that would have gone in the next step's
+// sub-step 0, those beyond a slice's slots, and slice 3, whose stage falls free at that barrier.
+template <int P8, bool TAIL, int AF, int BF, int BN>
+__device__ __forceinline__ void mx_step(Pipe<AF, BF, BN>& P, const ResTail<BN>& R,
+                                        uint8_t* const (&st)[kStages],
                                         v16f (&acc)[Shape<BN>::kTM][Shape<BN>::kTN], int k0,
                                         int kl, int k_end) {
   using PP = Pipe<AF, BF, BN>;
+  using RT = ResTail<BN>;
+  constexpr bool kLast = TAIL && P8 == 7;
+  constexpr int kM = PP::kCp < RT::kPer ? PP::kCp : RT::kPer;   // slots that carry residual
+  constexpr int kC3 = PP::cut(3);
+  constexpr int kLeft = RT::kPer - kM;                           // per slice, beyond the slots
+  constexpr int kPart3 = kM > kC3 ? kM - kC3 : 0;                // slice 2's sub-step-0 part
+  constexpr int kExtra = kLast ? 3 * kLeft + kPart3 + RT::kPer : 0;
   constexpr int TM = PP::TM, TN = PP::TN, NM = TM * TN;
   constexpr int ST = P8 % kStages;
   constexpr int ST1 = (ST + 1) % kStages;
@@ -267,15 +337,18 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF, BN>& P, uint8_t* const (&st
     constexpr int ds = (s + 1) & 3;          // sub-step decoded (s == 3: the next step's 0)
     constexpr int dpar = s == 3 ? PAR1 : PAR;
     // raw reads of the next step: unit 0 (and the one E2M1 unit) in s = 1, unit 1 in s = 2
-    constexpr int kRdA = s == 1 || (s == 2 && kByteA) ? TM : 0;
-    constexpr int kRdB = s == 1 || (s == 2 && kByteB) ? TN : 0;
-    constexpr int kScl = s == 3 ? 1 : 0;
-    constexpr int kDec = TM + TN;
+    constexpr int kRdA = !kLast && (s == 1 || (s == 2 && kByteA)) ? TM : 0;
+    constexpr int kRdB = !kLast && (s == 1 || (s == 2 && kByteB)) ? TN : 0;
+    constexpr int kScl = s == 3 && !kLast ? 1 : 0;
+    constexpr int kDec = s == 3 && kLast ? 0 : TM + TN;
     constexpr int c0 = s == 0 ? PP::cut(3) : PP::cut(s - 1);
     constexpr int c1 = s == 0 ? PP::kCp : PP::cut(s);
     constexpr int kCpy = c1 - c0;
-    constexpr int kSld = (s == 2 && SP == 0) ? TM + TN : 0;
-    constexpr int kTasks = kRdA + kRdB + kScl + kDec + kCpy + kSld;
+    constexpr int e0 = s == 0 ? 0 : (s - 1) * kExtra / 3, e1 = s == 0 ? 0 : s * kExtra / 3;
+    constexpr int kExt = e1 - e0;
+    // (TAIL: no scale bytes for the group past the range, whose step 4 would load them)
+    constexpr int kSld = (s == 2 && SP == 0 && !(TAIL && P8 == 4)) ? TM + TN : 0;
+    constexpr int kTasks = kRdA + kRdB + kScl + kDec + kCpy + kExt + kSld;
     auto task = [&](auto tc) {
       constexpr int t = decltype(tc)::value;
       if constexpr (t < kRdA) {
@@ -296,10 +369,24 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF, BN>& P, uint8_t* const (&st
         }
       } else if constexpr (t < kRdA + kRdB + kScl + kDec + kCpy) {
         constexpr int c = c0 + t - (kRdA + kRdB + kScl + kDec);
-        if constexpr (s >= 1) P.template copy<c>(st[(ST + 3) % kStages], kabs + 3, oob3);
-        else P.template copy<c>(st[(ST + 2) % kStages], kabs + 2, oob2);
+        if constexpr (s >= 1) {
+          if constexpr (TAIL && P8 >= 5) R.template issue<c, PP::kCp>(st[(ST + 3) % kStages], P8 - 5);
+          else P.template copy<c>(st[(ST + 3) % kStages], kabs + 3, oob3);
+        } else {
+          if constexpr (TAIL && P8 >= 6) R.template issue<c, PP::kCp>(st[(ST + 2) % kStages], P8 - 6);
+          else P.template copy<c>(st[(ST + 2) % kStages], kabs + 2, oob2);
+        }
+      } else if constexpr (t < kRdA + kRdB + kScl + kDec + kCpy + kExt) {
+        // residual copies without a slot (kLast): slices 0-2 beyond their slots, slice 2's
+        // sub-step-0 part, then slice 3
+        constexpr int e = e0 + t - (kRdA + kRdB + kScl + kDec + kCpy);
+        constexpr int sl = e < 3 * kLeft ? e / kLeft : e < 3 * kLeft + kPart3 ? 2 : 3;
+        constexpr int c = e < 3 * kLeft ? kM + e % kLeft
+                          : e < 3 * kLeft + kPart3 ? kC3 + (e - 3 * kLeft)
+                                                   : e - 3 * kLeft - kPart3;
+        R.template issue<c, PP::kCp>(st[sl], sl);
       } else {
-        constexpr int q = t - (kRdA + kRdB + kScl + kDec + kCpy);
+        constexpr int q = t - (kRdA + kRdB + kScl + kDec + kCpy + kExt);
         if constexpr (q < TM) P.fa.template load_group<GP ^ 1, q>(kabs + 4, oobg);
         else P.fb.template load_group<GP ^ 1, q - TM>(kabs + 4, oobg);
       }
@@ -317,7 +404,7 @@ __device__ __forceinline__ void mx_step(Pipe<AF, BF, BN>& P, uint8_t* const (&st
       // loads of the window since the previous barrier, i.e. the copies of step kl + 2 and the
       // scale group the previous step issued, if it did.  And every read of the stages the
       // copies of this window overwrite is done.
-      constexpr int kAfter = PP::kCp + ((P8 + 7) % 4 == 0 ? TM + TN : 0);
+      constexpr int kAfter = PP::kCp + ((P8 + 7) % 4 == 0 && !(TAIL && P8 == 5) ? TM + TN : 0);
       static_assert(kAfter < 64, "vmcnt field");
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kAfter));
       __builtin_amdgcn_s_barrier();
@@ -421,14 +508,27 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
     P.opb[0][j] = P.fb.template decode<0, j, 0>();
   });
 
-  for (int kl = 0; kl < KT; kl += 8) {
+  // The residual epilogue runs the range's last 8 steps apart (TAIL), to bring in the residual
+  // tile while they run.
+  constexpr bool kResTail = EPI == kEpiResidual && !SPLIT && !QUANT;
+  ResTail<BN> R;
+  R.on = false;
+  if constexpr (kResTail) R.init(p, m0, n0, bz, wave, lane);
+  int kl = 0;
+  for (; kl < KT - (kResTail ? 8 : 0); kl += 8) {
     static_for<0, 8>([&](auto pc) {
       constexpr int p8 = decltype(pc)::value;
-      mx_step<p8, AF, BF, BN>(P, st, acc, k0, kl + p8, k_end);
+      mx_step<p8, false, AF, BF, BN>(P, R, st, acc, k0, kl + p8, k_end);
     });
   }
-  // The copies issued for steps past the range may still be landing in the stages the
-  // epilogue reuses.
+  if constexpr (kResTail) {
+    static_for<0, 8>([&](auto pc) {
+      constexpr int p8 = decltype(pc)::value;
+      mx_step<p8, true, AF, BF, BN>(P, R, st, acc, k0, kl + p8, k_end);
+    });
+  }
+  // The copies issued for steps past the range (or the residual's) may still be landing in the
+  // stages the epilogue reuses.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
 
   auto tile_row = [&](int r) -> uint8_t* {
@@ -437,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(Args p) {
   };
   finish_tile<AF, QUANT, EPI, SPLIT, kTile, BN, SH::kWM, SH::kWN>(p, acc, tile_row, lds_bias,
                                                                   has_bias, split, tile_id, m0,
-                                                                  n0, bz);
+                                                                  n0, bz, R.on);
 }
 
 template <int AF, int BF, bool BIAS, bool QUANT, int EPI, bool SPLIT, int BN = kTile>
