@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmx_gfx950.so")
 
 SOURCES = ["mx_api.cpp", "act_quant.hip", "quant_transpose.hip", "gemm_fp4.hip", "gemm_bf16.hip",
-           "gemm_mx.hip", "gemm_scratch.hip"]
+           "gemm_mx.hip", "gemm_small.hip", "gemm_scratch.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

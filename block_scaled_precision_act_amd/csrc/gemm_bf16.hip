@@ -602,6 +602,11 @@ hipError_t launch_formats(const GemmProblem& g, const DeviceInfo& dev, hipStream
     return launch_tile<AF, BF, 256, 256, 2, 4>(g, dev.device, stream);
   }
   if (tiles(128, 128) >= cus) return launch_tile<AF, BF, 128, 128, 2, 2>(g, dev.device, stream);
+  // 64x64 tiles: with K of at most four chunks of 256 and one wave of workgroups, the kernel that
+  // copies the tile's whole K into LDS at the start (gemm_small.hip) instead of staging it a step
+  // at a time.  Its LDS (up to 128 KB) holds one workgroup per CU, so past one wave the step-wise
+  // kernel, several of whose workgroups share a CU, is faster (measured).
+  if (small_kernel_takes(g.K) && tiles(64, 64) <= cus) return launch_gemm_small(AF, BF, g, stream);
   return launch_tile<AF, BF, 64, 64, 2, 2>(g, dev.device, stream);
 }
 

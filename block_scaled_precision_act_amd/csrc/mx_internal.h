@@ -112,6 +112,11 @@ inline bool mx_kernel_takes(int64_t K, int splits) {
 hipError_t launch_gemm_mx(int a_fmt, int b_fmt, const GemmProblem& p, const SplitPlan* plan,
                           int tile_n, hipStream_t stream);
 
+// GEMM kernel for problems with few output tiles and a short K (gemm_small.hip): 64 x 64 tiles
+// whose whole K of operand codes is copied into LDS at the start, in chunks of 256, at most four.
+inline bool small_kernel_takes(int64_t K) { return K > 0 && K % 256 == 0 && K <= 1024; }
+hipError_t launch_gemm_small(int a_fmt, int b_fmt, const GemmProblem& p, hipStream_t stream);
+
 // Output tile width for that kernel: 224 where the problem's tiles of 256 x 224 fill the CUs'
 // waves enough better than 256 x 256 tiles do to finish sooner, counting a wave of the narrower
 // tiles as 224/256 of a wave of the wider (e.g. 4096 x 7168: 448 tiles of 256 x 256 take two
