@@ -203,28 +203,42 @@ __global__ __launch_bounds__(kSmThreads) void gemm_small_kernel(Args p) {
   __builtin_amdgcn_sched_barrier(0);
   if (has_bias && threadIdx.x < kSmTile) lds_bias[threadIdx.x] = bf16_bits_to_f32(bias_bits);
 
-  v16f acc = v16f{};
-  static_for<0, kSmChunks>([&](auto cc) {
+  // Steps t = 4c + s of K; step t + 1's raw codes are read before step t is decoded and
+  // contracted, so the LDS latency hides behind step t's MFMAs; chunk c + 1's wait and barrier
+  // come just before its first read.
+  using FA = SmFrag<AF, false>;
+  using FB = SmFrag<BF, BF == kFp8>;
+  uint4 ra[2][FA::kUnits], rb[2][FB::kUnits];
+  // this wavefront's copies of chunk c (and the scale bytes before them) have landed; past the
+  // barrier, every wavefront's have
+  auto chunk_ready = [&](auto cc) {
     constexpr int c = decltype(cc)::value;
+    __builtin_amdgcn_s_waitcnt(sm_waitcnt_vm((kSmChunks - 1 - c) * kCp));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  chunk_ready(IntC<0>{});
+  fa.template read<0>(ch[0], ra[0]);
+  fb.template read<0>(ch[0], rb[0]);
+  v16f acc = v16f{};
+  static_for<0, 4 * kSmChunks>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    constexpr int c = t / 4, s = t % 4;
     if (c < nch) {
-      // this wavefront's copies of chunk c (and the scale bytes before them) have landed; past
-      // the barrier, every wavefront's have
-      __builtin_amdgcn_s_waitcnt(sm_waitcnt_vm((kSmChunks - 1 - c) * kCp));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      static_for<0, 4>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        constexpr int t = 4 * c + s;
-        uint4 ra[SmFrag<AF, false>::kUnits], rb[SmFrag<BF, BF == kFp8>::kUnits];
-        fa.template read<s>(ch[c], ra);
-        fb.template read<s>(ch[c], rb);
-        const float sa = fa.template scale<t>(), sb = fb.template scale<t>();
-        static_for<0, 4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          const bf16x8 av = SmFrag<AF, false>::template decode<q>(ra, sa);
-          const bf16x8 bv = SmFrag<BF, BF == kFp8>::template decode<q>(rb, sb);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, acc, 0, 0, 0);
-        });
+      constexpr int t1 = t + 1, c1 = t1 / 4;
+      if constexpr (t1 < 4 * kSmChunks) {
+        if (c1 < nch) {
+          if constexpr (t1 % 4 == 0) chunk_ready(IntC<c1>{});
+          fa.template read<t1 % 4>(ch[c1], ra[t1 & 1]);
+          fb.template read<t1 % 4>(ch[c1], rb[t1 & 1]);
+        }
+      }
+      const float sa = fa.template scale<t>(), sb = fb.template scale<t>();
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const bf16x8 av = FA::template decode<q>(ra[t & 1], sa);
+        const bf16x8 bv = FB::template decode<q>(rb[t & 1], sb);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, acc, 0, 0, 0);
       });
     }
   });
