@@ -518,17 +518,27 @@ hipError_t launch_skinny_lds(const GemmProblem& g, hipStream_t stream) {
 }
 
 template <int MT>
-hipError_t launch_skinny_mt(const GemmProblem& g, hipStream_t stream) {
+hipError_t launch_skinny_mt(const GemmProblem& g, int cus, hipStream_t stream) {
   const int kt = (g.K + 127) / 128;
   if (g.K % 256 == 0) {
     // Codes staged through LDS.  Wavefronts: one chunk of 2 steps each for up to 12 steps of K (4 or 6 wavefronts, one
     // chunk buffer), else 8 with a ring of two buffers where those fit in 128 KB of LDS
     // (16 (MT + NC) rows x 128 bytes each), else 4.
-    if (g.q) {
-      if (kt <= 8) return launch_skinny_lds<MT, 2, 4, false, true>(g, stream);
-      if (kt <= 12) return launch_skinny_lds<MT, 2, 6, false, true>(g, stream);
-      if constexpr (MT + 2 <= 4) return launch_skinny_lds<MT, 2, 8, true, true>(g, stream);
-      return launch_skinny_lds<MT, 2, 4, true, true>(g, stream);
+    // 32 columns per workgroup where 16-column workgroups would not fit in one wave of the CUs:
+    // a CU then copies A's rows once for 32 columns instead of once per 16 (a CU running two
+    // 16-column workgroups copies them twice).
+    const int64_t wg16 = static_cast<int64_t>((g.N + 15) / 16) * g.batch;
+    if (g.q || wg16 > cus) {
+      if (g.q) {
+        if (kt <= 8) return launch_skinny_lds<MT, 2, 4, false, true>(g, stream);
+        if (kt <= 12) return launch_skinny_lds<MT, 2, 6, false, true>(g, stream);
+        if constexpr (MT + 2 <= 4) return launch_skinny_lds<MT, 2, 8, true, true>(g, stream);
+        return launch_skinny_lds<MT, 2, 4, true, true>(g, stream);
+      }
+      if (kt <= 8) return launch_skinny_lds<MT, 2, 4, false, false>(g, stream);
+      if (kt <= 12) return launch_skinny_lds<MT, 2, 6, false, false>(g, stream);
+      if constexpr (MT + 2 <= 4) return launch_skinny_lds<MT, 2, 8, true, false>(g, stream);
+      return launch_skinny_lds<MT, 2, 4, true, false>(g, stream);
     }
     if (kt <= 8) return launch_skinny_lds<MT, 1, 4, false, false>(g, stream);
     if (kt <= 12) return launch_skinny_lds<MT, 1, 6, false, false>(g, stream);
@@ -545,12 +555,12 @@ hipError_t launch_skinny_mt(const GemmProblem& g, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream) {
-  // Skinny problems only (M <= 64): 16-column workgroups with split K.
-  if (p.M <= 16) return launch_skinny_mt<1>(p, stream);
-  if (p.M <= 32) return launch_skinny_mt<2>(p, stream);
-  if (p.M <= 48) return launch_skinny_mt<3>(p, stream);
-  return launch_skinny_mt<4>(p, stream);
+hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, int cus, hipStream_t stream) {
+  // Skinny problems only (M <= 64): 16- or 32-column workgroups with split K.
+  if (p.M <= 16) return launch_skinny_mt<1>(p, cus, stream);
+  if (p.M <= 32) return launch_skinny_mt<2>(p, cus, stream);
+  if (p.M <= 48) return launch_skinny_mt<3>(p, cus, stream);
+  return launch_skinny_mt<4>(p, cus, stream);
 }
 
 hipError_t launch_gemm(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceInfo& dev,
@@ -558,7 +568,8 @@ hipError_t launch_gemm(int a_fmt, int b_fmt, const GemmProblem& p, const DeviceI
   // Both operands MXFP4: the scaled FP4 MFMA for the skinny (decode-like) shapes, M <= 64; from
   // M = 65 on, the tiled bf16-decode kernel (3.7x faster at 4096x7168x2048 than one wavefront
   // per 32x32 tile of the scaled FP4 MFMA, as first built here).
-  if (a_fmt == kFp4 && b_fmt == kFp4 && p.M <= 64) return launch_gemm_fp4_mfma(p, stream);
+  if (a_fmt == kFp4 && b_fmt == kFp4 && p.M <= 64)
+    return launch_gemm_fp4_mfma(p, dev.cu_count > 0 ? dev.cu_count : 256, stream);
   return launch_gemm_bf16(a_fmt, b_fmt, p, dev, stream);
 }
 

@@ -130,7 +130,7 @@ inline int mx_tile_n(int64_t M, int64_t N, int64_t batch, int64_t cus) {
   return waves(224) * 224 < waves(256) * 256 ? 224 : 256;
 }
 // Both operands MXFP4 on the scaled f8f6f4 MFMA (gemm_fp4.hip).
-hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_gemm_fp4_mfma(const GemmProblem& p, int cus, hipStream_t stream);
 
 // The split GEMM of p on this library's fixed device array instead of p.workspace (which it
 // ignores), for callers that cannot allocate (gemm_scratch.hip); no_alloc_scratch_bytes() is the

@@ -4,8 +4,9 @@ against the oracle.
 Every case is a shape that takes that kernel: M <= 64 and K % 256 == 0.  Its three launch forms
 are all covered: one 2-step chunk per wavefront with 4 wavefronts (up to 8 steps of K) or 6 (up
 to 12), and the two-buffer ring of 8 wavefronts (or 4 when 64 rows and 32 columns would not fit)
-for longer K, whose wavefronts each take several chunks.  Ragged M (every tile count 1-4, rows
-past M in the last tile) and N (columns past N in the last workgroup), batches, the bias, the
+for longer K, whose wavefronts each take several chunks; 16-column workgroups, and 32-column ones
+where the 16-column grid would not fit in one wave of the CUs.  Ragged M (every tile count 1-4,
+rows past M in the last tile) and N (columns past N in the last workgroup), batches, the bias, the
 residual and GELU epilogues, and the MXFP4-quantized output.  Each output is checked against
 the float64 reference of the same bytes within |out - ref| <= 2^-7 |ref| + 2^-20 sum_k |a_k b_k|
 (the GELU and quantized outputs within the bounds their oracles derive).
@@ -28,6 +29,11 @@ def takes_lds_kernel(M, K):
     return M <= 64 and K % 256 == 0
 
 
+def wide_workgroups(N, batch=1, cus=256):
+    """32 columns per workgroup: where 16-column workgroups would not fit in one wave."""
+    return -(-N // 16) * batch > cus
+
+
 SHAPES = [(1, 1, 256), (16, 16, 512), (17, 33, 1024), (33, 200, 1536), (41, 4607, 1536),
           (48, 100, 768), (64, 130, 2048), (41, 96, 3072), (64, 64, 6144), (9, 1537, 6144),
           (41, 300, 4096)]
@@ -42,10 +48,22 @@ def test_shapes_against_oracle(mx, M, N, K, with_bias):
     check_workload(mx, w)
 
 
-@pytest.mark.parametrize("M,N,K", [(41, 96, 1536), (20, 70, 4096)])
+@pytest.mark.parametrize("M,N,K", [(41, 96, 1536), (20, 70, 4096), (20, 2000, 1024)])
 def test_batched(mx, M, N, K):
     w = synth.gemm_inputs("fp4", "fp4", M, N, K, seed=M + N + K, batch=3, with_bias=True)
     check_workload(mx, w)
+
+
+# 32-column workgroups (more 16-column workgroups than CUs): ragged N (a workgroup with 16 or
+# fewer live columns), every tile count, one buffer and the ring
+@pytest.mark.parametrize("M,N,K", [(41, 4608, 1536), (41, 6144, 1536), (41, 4100, 1536),
+                                   (16, 4111, 512), (64, 5000, 1024), (33, 8192, 3072),
+                                   (48, 4200, 6144)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_wide_workgroups(mx, M, N, K, with_bias):
+    assert takes_lds_kernel(M, K) and wide_workgroups(N)
+    check_workload(mx, synth.gemm_inputs("fp4", "fp4", M, N, K, seed=3 * M + N + K + with_bias,
+                                         with_bias=with_bias))
 
 
 @pytest.mark.parametrize("M,N,K", [(41, 4608, 1536), (41, 1536, 6144)])
@@ -56,7 +74,7 @@ def test_headline_shapes_take_it(mx, M, N, K):
 
 
 @pytest.mark.parametrize("epi", ["residual", "gelu"])
-@pytest.mark.parametrize("M,N,K", [(41, 200, 1536), (64, 96, 6144)])
+@pytest.mark.parametrize("M,N,K", [(41, 200, 1536), (64, 96, 6144), (41, 4100, 1536)])
 def test_epilogues(mx, epi, M, N, K):
     w = synth.gemm_inputs("fp4", "fp4", M, N, K, seed=M + 5 * N + K, with_bias=True)
     a, a_s, _, A, B, bias = operands(w)
