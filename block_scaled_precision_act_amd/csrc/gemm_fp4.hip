@@ -48,9 +48,10 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
 // (l % 16) and K-block g = l / 16 of the 128-wide K step, 16 bytes = 32 E2M1 codes (low nibble
 // first) in dwords 0..3, and passes that block's E8M0 byte; accumulator register r of lane l is
 // C[4 * (l / 16) + r][l % 16].
-// A workgroup owns 16 output columns and all M rows (MT tiles of 16); its W wavefronts split the
-// K steps into contiguous ranges and load a group of up to G steps at once (one memory round
-// trip per group).  The per-wave partial sums are added in LDS in wave order (deterministic),
+// A workgroup owns 16 output columns and all M rows (MT tiles of 16), or half of the row tiles
+// (the codes staged through LDS, with room for twice the workgroups in one wave); its W
+// wavefronts split the K steps into contiguous ranges and load a group of up to G steps at once
+// (one memory round trip per group).  The per-wave partial sums are added in LDS in wave order (deterministic),
 // then the bias is added in fp32 and each output is rounded once to bf16.  Rows past M and
 // columns past N read zeros through the buffer bound; K blocks past K read zeros through an
 // out-of-range offset.
@@ -67,7 +68,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_
 // once to bf16; or, QUANT, the bf16 results are quantized to MXFP4 per 32 columns.
 template <int MT, int NC, int W, bool BIAS, int EPI, bool QUANT>
 __device__ __forceinline__ void skinny_finish(const Args& p, v4f (&acc)[MT][NC], v4f* red, int wave,
-                                              int lane, int n0, int64_t bz) {
+                                              int lane, int m0, int n0, int64_t bz) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 #pragma unroll
@@ -106,11 +107,12 @@ __device__ __forceinline__ void skinny_finish(const Args& p, v4f (&acc)[MT][NC],
     const uint16_t* res = p.res + bz * p.stride_res;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * t + 4 * g + r;
+      const int lrow = 16 * t + 4 * g + r;       // row within the workgroup's rows
+      const int row = m0 + lrow;
       float v = sums[i][r] + bias;
       if constexpr (QUANT) {
         if constexpr (EPI == kEpiGelu) v = gelu_f32(v);
-        stage[row][16 * c + r16] = to_bf16(v);
+        stage[lrow][16 * c + r16] = to_bf16(v);
       } else {
         if (row >= p.M) continue;
         const int64_t at = static_cast<int64_t>(row) * p.N + col;
@@ -126,8 +128,9 @@ __device__ __forceinline__ void skinny_finish(const Args& p, v4f (&acc)[MT][NC],
     __syncthreads();
     const int idx = threadIdx.x;                // row idx / 4, columns 8 (idx % 4) .. + 8
     if (idx < 16 * MT * 4) {                    // whole quads: the DPP max stays inside
-      const int row = idx >> 2, ch = idx & 3;
-      const uint4 v = *reinterpret_cast<const uint4*>(&stage[row][8 * ch]);
+      const int lrow = idx >> 2, ch = idx & 3;
+      const int row = m0 + lrow;
+      const uint4 v = *reinterpret_cast<const uint4*>(&stage[lrow][8 * ch]);
       const QuantChunkFp4 qc = quant_chunk_fp4(v);
       if (row < p.M) {
         uint8_t* q = p.q + bz * p.stride_q;
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_kernel(Args p) {
     }
   }
 
-  skinny_finish<MT, NC, W, BIAS, EPI, QUANT>(p, acc, &red[0][0][0][0], wave, lane, n0, bz);
+  skinny_finish<MT, NC, W, BIAS, EPI, QUANT>(p, acc, &red[0][0][0][0], wave, lane, 0, n0, bz);
 }
 
 // The same GEMM with its codes staged through LDS (K % 256 == 0).  A fragment load of the
@@ -312,6 +315,7 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_lds_kernel(Args p) {
   const int g = lane >> 4;
   const int64_t bz = blockIdx.y;
   const int n0 = blockIdx.x * 16 * NC;
+  const int m0 = blockIdx.z * 16 * MT;           // the workgroup's rows of A (and C)
   const int pitch = p.K / 2;
   const int kb_total = p.K / 32;
   const int KT = p.K / 128;                      // even: K % 256 == 0
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_lds_kernel(Args p) {
     const int r = 8 * i + (lane >> 3);           // row within the chunk
     const int u = (lane & 7) ^ ((r >> 1) & 7);
     const bool is_a = i < 2 * MT;
-    const int row = is_a ? r : n0 + r - 16 * MT;
+    const int row = is_a ? m0 + r : n0 + r - 16 * MT;
     const int lim = is_a ? p.M : p.N;
     cp_off[i] = row < lim ? static_cast<uint32_t>(row) * pitch + 16u * u : 0x80000000u;
   }
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_lds_kernel(Args p) {
   uint32_t as_row[MT], bs_row[NC];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int row = 16 * t + r16;
+    const int row = m0 + 16 * t + r16;
     as_row[t] = row < p.M ? static_cast<uint32_t>(row) * kb_total : 0x80000000u;
   }
 #pragma unroll
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(64 * W) void gemm_fp4_skinny_lds_kernel(Args p) {
   // every wavefront is past its last operand read (skinny_finish's first barrier precedes any
   // read of `red`, and every copy has landed: the last chunk waited for vmcnt 0)
   __syncthreads();
-  skinny_finish<MT, NC, W, BIAS, EPI, QUANT>(p, acc, reinterpret_cast<v4f*>(buf0), wave, lane, n0, bz);
+  skinny_finish<MT, NC, W, BIAS, EPI, QUANT>(p, acc, reinterpret_cast<v4f*>(buf0), wave, lane, m0, n0, bz);
 }
 
 template <int MT, int NC, int W, int G>
@@ -484,11 +488,11 @@ hipError_t launch_skinny(const GemmProblem& g, hipStream_t stream) {
 
 
 template <int MT, int NC, int W, bool RING, bool QUANT>
-hipError_t launch_skinny_lds(const GemmProblem& g, hipStream_t stream) {
+hipError_t launch_skinny_lds(const GemmProblem& g, hipStream_t stream, int mgroups = 1) {
   Args p{g.a, g.a_s, g.b, g.b_s, g.bias, g.c, g.M, g.N, g.K,
          g.stride_a, g.stride_as, g.stride_b, g.stride_bs, g.stride_bias, g.stride_c,
          g.residual, g.stride_res, g.q, g.qs, g.stride_q, g.stride_qs};
-  const dim3 grid((g.N + 16 * NC - 1) / (16 * NC), g.batch);
+  const dim3 grid((g.N + 16 * NC - 1) / (16 * NC), g.batch, mgroups);
   const dim3 block(64 * W);
   if constexpr (QUANT) {
     if (g.epi == kEpiGelu)
@@ -517,6 +521,17 @@ hipError_t launch_skinny_lds(const GemmProblem& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The LDS kernel with 16-column workgroups of MT row tiles each and `mgroups` workgroups per
+// column block (row tiles [MT i, MT i + MT) in workgroup i).
+template <int MT>
+hipError_t launch_skinny_lds_rows(const GemmProblem& g, int mgroups, hipStream_t stream) {
+  const int kt = (g.K + 127) / 128;
+  if (kt <= 8) return launch_skinny_lds<MT, 1, 4, false, false>(g, stream, mgroups);
+  if (kt <= 12) return launch_skinny_lds<MT, 1, 6, false, false>(g, stream, mgroups);
+  if constexpr (MT + 1 <= 4) return launch_skinny_lds<MT, 1, 8, true, false>(g, stream, mgroups);
+  return launch_skinny_lds<MT, 1, 4, true, false>(g, stream, mgroups);
+}
+
 template <int MT>
 hipError_t launch_skinny_mt(const GemmProblem& g, int cus, hipStream_t stream) {
   const int kt = (g.K + 127) / 128;
@@ -528,6 +543,11 @@ hipError_t launch_skinny_mt(const GemmProblem& g, int cus, hipStream_t stream) {
     // a CU then copies A's rows once for 32 columns instead of once per 16 (a CU running two
     // 16-column workgroups copies them twice).
     const int64_t wg16 = static_cast<int64_t>((g.N + 15) / 16) * g.batch;
+    // Where even twice the 16-column grid fits in one wave, two workgroups per column block,
+    // each with half the row tiles: a CU copies half of A's rows (plus the block's B rows).
+    if constexpr (MT >= 2) {
+      if (!g.q && 2 * wg16 <= cus) return launch_skinny_lds_rows<(MT + 1) / 2>(g, 2, stream);
+    }
     if (g.q || wg16 > cus) {
       if (g.q) {
         if (kt <= 8) return launch_skinny_lds<MT, 2, 4, false, true>(g, stream);
@@ -540,10 +560,7 @@ hipError_t launch_skinny_mt(const GemmProblem& g, int cus, hipStream_t stream) {
       if constexpr (MT + 2 <= 4) return launch_skinny_lds<MT, 2, 8, true, false>(g, stream);
       return launch_skinny_lds<MT, 2, 4, true, false>(g, stream);
     }
-    if (kt <= 8) return launch_skinny_lds<MT, 1, 4, false, false>(g, stream);
-    if (kt <= 12) return launch_skinny_lds<MT, 1, 6, false, false>(g, stream);
-    if constexpr (MT + 1 <= 4) return launch_skinny_lds<MT, 1, 8, true, false>(g, stream);
-    return launch_skinny_lds<MT, 1, 4, true, false>(g, stream);
+    return launch_skinny_lds_rows<MT>(g, 1, stream);
   }
   if (g.q) {   // quantized output: 32 columns per workgroup (one scale block of each row)
     if (kt >= 32) return launch_skinny<MT, 2, 8, 4, true>(g, stream);

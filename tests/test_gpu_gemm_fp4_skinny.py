@@ -5,7 +5,9 @@ Every case is a shape that takes that kernel: M <= 64 and K % 256 == 0.  Its thr
 are all covered: one 2-step chunk per wavefront with 4 wavefronts (up to 8 steps of K) or 6 (up
 to 12), and the two-buffer ring of 8 wavefronts (or 4 when 64 rows and 32 columns would not fit)
 for longer K, whose wavefronts each take several chunks; 16-column workgroups, and 32-column ones
-where the 16-column grid would not fit in one wave of the CUs.  Ragged M (every tile count 1-4,
+where the 16-column grid would not fit in one wave of the CUs; and, where twice the 16-column
+grid fits in one wave (and M > 16), two workgroups per column block with half the row tiles each
+(the second one's last tile partly or wholly past M).  Ragged M (every tile count 1-4,
 rows past M in the last tile) and N (columns past N in the last workgroup), batches, the bias, the
 residual and GELU epilogues, and the MXFP4-quantized output.  Each output is checked against
 the float64 reference of the same bytes within |out - ref| <= 2^-7 |ref| + 2^-20 sum_k |a_k b_k|
@@ -32,6 +34,16 @@ def takes_lds_kernel(M, K):
 def wide_workgroups(N, batch=1, cus=256):
     """32 columns per workgroup: where 16-column workgroups would not fit in one wave."""
     return -(-N // 16) * batch > cus
+
+
+def row_split(M, N, batch=1, cus=256):
+    """Two workgroups per column block, half the row tiles each (the plain and epilogue forms)."""
+    return M > 16 and 2 * -(-N // 16) * batch <= cus
+
+
+def test_headline_rules():
+    assert row_split(41, 1536) and not row_split(41, 4608) and wide_workgroups(4608)
+    assert not row_split(16, 1000) and row_split(17, 33)
 
 
 SHAPES = [(1, 1, 256), (16, 16, 512), (17, 33, 1024), (33, 200, 1536), (41, 4607, 1536),
