@@ -440,7 +440,8 @@ __device__ __forceinline__ void finish_tile(const Args& p, v16f (&acc)[BM / WM /
       for (int it = 0; it < kIters; ++it) {
         const int idx = static_cast<int>(threadIdx.x) + it * NT;
         const int trow = idx / kChunksPerRow, tch = idx % kChunksPerRow;
-        *reinterpret_cast<uint4*>(c + static_cast<int64_t>(m0 + trow) * p.N + n0 + tch * 8) = v[it];
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v[it]), reinterpret_cast<v4u*>(
+            c + static_cast<int64_t>(m0 + trow) * p.N + n0 + tch * 8));
       }
     } else {
       for (int idx = threadIdx.x; idx < BM * kChunksPerRow; idx += NT) {

@@ -61,6 +61,7 @@ CASES = [("acts", "fp4", 4096, 7168, 2048, None, 224),   # the headline shape: 6
          ("acts", "fp8", 2000, 7000, 512, None, 224),    # 8 slots, 7 copies; K of one group;
                                                           # ragged M and N
          ("acts", "fp8", 4000, 4096, 1024, None, 256),   # 8 slots, 8 copies; ragged M
+         ("fp4", "fp4", 4096, 4096, 1024, None, 256),    # 4 slots, 8 copies
          ("acts", "fp4", 1024, 7000, 512, 2, 224)]       # a batch sharing one residual
 
 
