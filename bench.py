@@ -955,17 +955,29 @@ BUSY_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM
                  "SQ_INSTS_MFMA")
 
 
+# the GEMMs whose MFMA utilisation the counter run records: profile key, title, kernel pattern,
+# dispatch grid in work-items (None: the only grid of that kernel in the run), batch, M, N, K
+BUSY_TARGETS = (
+    ("gemm_fp8_fp4_4096x7168x2048", "the FP8xMXFP4 GEMM 4096x7168x2048 + bias",
+     GEMM_FP8_FP4_KERNEL, None, 1, 4096, 7168, 2048),
+    ("gemm_fp8_fp8_8192cubed", "the FP8xFP8 GEMM 8192^3",
+     GEMM_FP8_FP8_KERNEL, 32 * 32 * GEMM_THREADS, 1, 8192, 8192, 8192),
+    ("gemm_fp8_fp8_batched_8x1024x2048x2048", "the FP8xFP8 GEMM 8 x 1024x2048x2048",
+     GEMM_FP8_FP8_KERNEL, 4 * 8 * GEMM_THREADS * 8, 8, 1024, 2048, 2048),
+)
+
+
 def summarize_busy(busy_dir, prof_dir=None):
-    """MFMA utilisation of the 4096x7168x2048 GEMM from one rocprofv3 --pmc run of BUSY_COUNTERS
-    with --kernel-trace (the trace gives each dispatch's duration).  Counter values in the csv are
-    sums over the XCDs and shader engines.  Per dispatch:
+    """MFMA utilisation of the large GEMMs (BUSY_TARGETS) from one rocprofv3 --pmc run of
+    BUSY_COUNTERS with --kernel-trace (the trace gives each dispatch's duration).  Counter values
+    in the csv are sums over the XCDs and shader engines.  Per dispatch:
     * active cycles g = GRBM_GUI_ACTIVE / XCDs (the GUI counter runs once per XCD), clock = g / ns;
     * mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (g * SIMDs), rocprofv3's own MfmaUtil;
     * cu_busy = SQ_BUSY_CU_CYCLES / (g * CUs), and mfma_busy_over_busy_cu = MFMA-busy cycles over
       the SIMD cycles of CUs that hold a workgroup.  SQ_BUSY_CU_CYCLES is read in plain cycles:
       read as quad-cycles it would exceed CUs * g threefold.
-    Medians over the dispatches are written to mfma_util_<kernel>.json and .txt in prof_dir
-    (profiles/ by default) and returned."""
+    Medians over each GEMM's dispatches are written to mfma_util_<key>.json and .txt in prof_dir
+    (profiles/ by default); the 4096x7168x2048 GEMM's figures are returned."""
     import csv
     import glob
     import statistics
@@ -978,52 +990,61 @@ def summarize_busy(busy_dir, prof_dir=None):
     simds, cus, xcds = int(agent["Simd_Count"]), int(agent["Cu_Count"]), int(agent["Num_Xcc"])
     dur = {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
            for r in rows("*kernel_trace.csv")}
-    ctr = {}
-    for r in rows("*counter_collection.csv"):
-        if re.search(GEMM_FP8_FP4_KERNEL, r["Kernel_Name"]):
-            ctr.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
-    per = []
-    for did, v in ctr.items():
-        if did not in dur or len(v) < len(BUSY_COUNTERS.split()):
-            continue
-        g = v["GRBM_GUI_ACTIVE"] / xcds
-        per.append({"duration_us": dur[did] / 1000.0, "clock_ghz": g / dur[did],
-                    "mfma_util": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds),
-                    "cu_busy": v["SQ_BUSY_CU_CYCLES"] / (g * cus),
-                    "mfma_busy_over_busy_cu": v["SQ_VALU_MFMA_BUSY_CYCLES"] /
-                                              (v["SQ_BUSY_CU_CYCLES"] * simds / cus),
-                    "mfma_insts": v["SQ_INSTS_MFMA"],
-                    "mfma_busy_cycles_per_inst": v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["SQ_INSTS_MFMA"]})
-    if not per:
-        print("no GEMM dispatches with every counter found", file=sys.stderr)
-        return None
-    med = {k: round(statistics.median(d[k] for d in per), 4) for k in per[0]}
-    M, N, K = 4096, 7168, 2048
+    counter_rows = rows("*counter_collection.csv")
     cmd = (f"rocprofv3 --pmc {BUSY_COUNTERS} --kernel-trace --output-format csv -d OUT/busy -o run "
            "-- python3 bench.py --counter-run")
-    out = {"source_hash": _kernel_hash(GEMM_SOURCES), "dispatches": len(per),
-           "simds": simds, "cus": cus, "xcds": xcds,
-           "mfma_insts_expected": 2 * M * N * K // (32 * 32 * 16 * 2), **med, "command": cmd}
     prof = prof_dir or os.path.join(HERE, "profiles")
-    name = "mfma_util_gemm_fp8_fp4_4096x7168x2048"
-    with open(os.path.join(prof, name + ".json"), "w") as fh:
-        json.dump(out, fh, indent=1)
-    txt = [f"MFMA utilisation of the FP8xMXFP4 GEMM 4096x7168x2048 + bias (bf16 MFMA 32x32x16),",
-           f"medians over {len(per)} dispatches of one counter run:", "",
-           "command (TMPDIR=/tmp, repository root as cwd, OUT the folder the profiler writes to):",
-           "  " + cmd, "  python bench.py --summarize-busy OUT/busy", "",
-           f"duration {med['duration_us']} us at {med['clock_ghz']} GHz "
-           f"(GRBM_GUI_ACTIVE over the {xcds} XCDs / duration)",
-           f"MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x {simds} SIMDs) = {med['mfma_util']}",
-           f"CUs holding a workgroup: {med['cu_busy']} of the active cycles; MFMA-busy over their "
-           f"SIMD cycles = {med['mfma_busy_over_busy_cu']}",
-           f"MFMA instructions {med['mfma_insts']:.0f} (2MNK/32768 = {out['mfma_insts_expected']}), "
-           f"{med['mfma_busy_cycles_per_inst']} busy cycles each",
-           f"source hash {out['source_hash']}"]
-    with open(os.path.join(prof, name + ".txt"), "w") as fh:
-        fh.write("\n".join(txt) + "\n")
-    print("\n".join(txt))
-    return out
+    result = None
+    for key, title, pattern, grid, batch, M, N, K in BUSY_TARGETS:
+        ctr = {}
+        for r in counter_rows:
+            if not re.search(pattern, r["Kernel_Name"]):
+                continue
+            if grid is not None and int(r.get("Grid_Size", -1)) != grid:
+                continue
+            ctr.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        per = []
+        for did, v in ctr.items():
+            if did not in dur or len(v) < len(BUSY_COUNTERS.split()):
+                continue
+            g = v["GRBM_GUI_ACTIVE"] / xcds
+            per.append({"duration_us": dur[did] / 1000.0, "clock_ghz": g / dur[did],
+                        "mfma_util": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds),
+                        "cu_busy": v["SQ_BUSY_CU_CYCLES"] / (g * cus),
+                        "mfma_busy_over_busy_cu": v["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                                  (v["SQ_BUSY_CU_CYCLES"] * simds / cus),
+                        "mfma_insts": v["SQ_INSTS_MFMA"],
+                        "mfma_busy_cycles_per_inst": v["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                                     v["SQ_INSTS_MFMA"]})
+        if not per:
+            print(f"{key}: no dispatches with every counter found", file=sys.stderr)
+            continue
+        med = {k: round(statistics.median(d[k] for d in per), 4) for k in per[0]}
+        out = {"source_hash": _kernel_hash(GEMM_SOURCES), "dispatches": len(per),
+               "simds": simds, "cus": cus, "xcds": xcds,
+               "mfma_insts_expected": 2 * batch * M * N * K // (32 * 32 * 16 * 2), **med,
+               "command": cmd}
+        with open(os.path.join(prof, f"mfma_util_{key}.json"), "w") as fh:
+            json.dump(out, fh, indent=1)
+        txt = [f"MFMA utilisation of {title} (bf16 MFMA 32x32x16),",
+               f"medians over {len(per)} dispatches of one counter run:", "",
+               "command (TMPDIR=/tmp, repository root as cwd, OUT the folder the profiler writes to):",
+               "  " + cmd, "  python bench.py --summarize-busy OUT/busy", "",
+               f"duration {med['duration_us']} us at {med['clock_ghz']} GHz "
+               f"(GRBM_GUI_ACTIVE over the {xcds} XCDs / duration)",
+               f"MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x {simds} SIMDs) = "
+               f"{med['mfma_util']}",
+               f"CUs holding a workgroup: {med['cu_busy']} of the active cycles; MFMA-busy over their "
+               f"SIMD cycles = {med['mfma_busy_over_busy_cu']}",
+               f"MFMA instructions {med['mfma_insts']:.0f} (2MNK/32768 = "
+               f"{out['mfma_insts_expected']}), {med['mfma_busy_cycles_per_inst']} busy cycles each",
+               f"source hash {out['source_hash']}"]
+        with open(os.path.join(prof, f"mfma_util_{key}.txt"), "w") as fh:
+            fh.write("\n".join(txt) + "\n")
+        print("\n".join(txt) + "\n")
+        if result is None and key == BUSY_TARGETS[0][0]:
+            result = out
+    return result
 
 
 if __name__ == "__main__":

@@ -81,3 +81,34 @@ def test_summarize_busy_arithmetic(tmp_path):
     assert abs(out["mfma_busy_over_busy_cu"] - 0.5 / 0.75) < 1e-3
     assert out["mfma_busy_cycles_per_inst"] == 32.0
     assert (tmp_path / "mfma_util_gemm_fp8_fp4_4096x7168x2048.json").exists()
+
+
+def test_summarize_busy_picks_the_fp8_gemms_by_grid(tmp_path):
+    """The 8192^3 and batched FP8 x FP8 GEMMs run one kernel; their profiles are told apart by the
+    dispatch grid (work-items) the counter csv records.  Each gets its own file, from its own
+    dispatches only: 8192^3 at MFMA util 0.25, the batched shape at 0.75."""
+    busy = tmp_path / "busy"
+    busy.mkdir()
+    _write_csv(busy / "run_agent_info.csv", ["Name", "Simd_Count", "Cu_Count", "Num_Xcc"],
+               [["gfx950", 1024, 256, 8]])
+    fp8 = ("void mx::(anonymous namespace)::gemm_mx_kernel<0, 0, false, false, 0, false, 256>"
+           "(mx::(anonymous namespace)::Args)")
+    _write_csv(busy / "run_kernel_trace.csv", ["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                                "End_Timestamp"],
+               [[1, fp8, 0, 100000], [2, fp8, 200000, 300000]])
+    g = 200000.0
+    rows = []
+    for d, grid, util in ((1, 32 * 32 * 256, 0.25), (2, 4 * 8 * 256 * 8, 0.75)):
+        counters = {"SQ_VALU_MFMA_BUSY_CYCLES": util * g * 1024, "SQ_BUSY_CYCLES": 1.0,
+                    "SQ_BUSY_CU_CYCLES": g * 256, "GRBM_GUI_ACTIVE": g * 8,
+                    "SQ_INSTS_MFMA": util * g * 1024 / 32}
+        rows += [[d, fp8, grid, name, v] for name, v in counters.items()]
+    _write_csv(busy / "run_counter_collection.csv",
+               ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"], rows)
+    bench.summarize_busy(str(busy), prof_dir=str(tmp_path))
+    for key, util in (("gemm_fp8_fp8_8192cubed", 0.25),
+                      ("gemm_fp8_fp8_batched_8x1024x2048x2048", 0.75)):
+        with open(tmp_path / f"mfma_util_{key}.json") as fh:
+            d = json.load(fh)
+        assert d["dispatches"] == 1 and abs(d["mfma_util"] - util) < 1e-4, key
+    assert not (tmp_path / "mfma_util_gemm_fp8_fp4_4096x7168x2048.json").exists()
