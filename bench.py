@@ -18,7 +18,9 @@ drop that sustained load brings), then 12 groups of 10 back-to-back launches, on
 events per group on the stream the launches go to; the figure is the median of the 12 group
 means (120 launches).  `roofline` is the dominant kernel (the 4096x7168x2048 GEMM) timed that
 way, against the dense FP8 MFMA peak.  `gemm_8192cubed` and `gemm_batched_8x1024x2048x2048` are
-the two large FP8 x FP8 configurations, each with its own roofline block.  `latency` holds the
+the two large FP8 x FP8 configurations, each with its own roofline block.  Each of the three large GEMM
+blocks also carries `cold_ms`: the median of 10 single launches, each after 512 MB were written to
+evict the caches (taken before the leg's timed launches).  `latency` holds the
 small configurations (16x256x512, 1024^3 + bias and the three skinny A4W4 shapes): the same
 median, `graph_ms` (20 launches captured in one HIP graph, replayed; launch overhead amortized)
 and `cold_ms` (median of single launches, each after 512 MB were written to evict the caches).
@@ -178,6 +180,30 @@ def timed(fn, torch):
     return ms, warm, GROUPS * PER_GROUP
 
 
+FLUSH_BYTES = 512 << 20        # written before each cold launch: twice the 256 MB last-level cache
+COLD_ITERS = 10               # cold launches per leg (none in a counter run)
+
+
+def cold_ms(fn, torch, flush, iters: int | None = None):
+    """Median over `iters` (default COLD_ITERS) single calls of fn, each after the whole `flush`
+    buffer (FLUSH_BYTES) was written, which evicts the L2s and the last-level cache: a pair of HIP
+    events on the current stream around the call alone.  None when there are no iterations."""
+    iters = COLD_ITERS if iters is None else iters
+    if iters <= 0:
+        return None
+    cur = torch.cuda.current_stream()
+    ts = []
+    for i in range(iters):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        fn()
+        b.record(cur)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return statistics.median(ts)
+
+
 def paired_ms(fns, torch):
     """Median ms per call of each of `fns`, timed in alternation so that every one sees the same
     clock and temperature (the clock of this GPU moves with its recent load): a settling phase
@@ -310,8 +336,8 @@ def main():
         summarize_busy(args.summarize_busy)
         return
     if args.counter_run:
-        global SETTLE_MS, GROUPS, PER_GROUP
-        SETTLE_MS, GROUPS, PER_GROUP = 0.0, 1, 2
+        global SETTLE_MS, GROUPS, PER_GROUP, COLD_ITERS
+        SETTLE_MS, GROUPS, PER_GROUP, COLD_ITERS = 0.0, 1, 2, 0
         args.steps, args.warmup, args.no_cpu = 2, 1, True
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this hot path has no "
@@ -381,7 +407,11 @@ def main():
     def gemm():
         mx.mx_gemm_fp8_fp4(q, s, b, b_s, c, bias=bias, stream=stream)
 
-    # the vendor comparison first, so that the leg's own timed launches are the last of the kernel
+    # the cold launches and the vendor comparison first, so that the leg's own timed launches are
+    # the last of the kernel
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    gemm_cold = cold_ms(gemm, torch, flush)
+    del flush
     vendor = vendor_pair(torch, gemm, None, M, N, K)
     gemm_ms, warm, n = timed(gemm, torch)
     tiles = ((M + 255) // 256) * ((N + C5_TILE_N - 1) // C5_TILE_N)
@@ -392,6 +422,7 @@ def main():
     out["gemm_only_tflops"] = out["roofline"]["achieved"]
     progress(f"gemm 4096x7168x2048: {gemm_ms * 1e3:.2f} us")
     out["roofline"]["vendor_bf16"] = vendor
+    out["roofline"]["cold_ms"] = None if gemm_cold is None else round(gemm_cold, 5)
     del x
 
     # ---- the two large FP8 x FP8 configurations (A quantized on the GPU by act_quant)
@@ -490,7 +521,11 @@ def bench_large(mx, synth, torch, dev_u8, dev_bf16, stream, w, profile_key):
     def gemm():
         mx.mx_gemm_fp8_fp8(a, a_s, b, b_s, c, stream=stream)
 
-    # the vendor comparison first, so that the leg's own timed launches are the last of the kernel
+    # the cold launches and the vendor comparison first, so that the leg's own timed launches are
+    # the last of the kernel and grid
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    cold = cold_ms(gemm, torch, flush)
+    del flush
     vendor = vendor_pair(torch, gemm, w.batch, w.M, w.N, w.K)
     ms, warm, n = timed(gemm, torch)
     flops = 2.0 * w.M * w.N * w.K * batch
@@ -502,6 +537,7 @@ def bench_large(mx, synth, torch, dev_u8, dev_bf16, stream, w, profile_key):
     block["workload"] = (f"FP8xFP8 GEMM {batch_txt}{w.M}x{w.N}x{w.K}, 32x32 block-scaled E4M3 "
                          f"weights, activations through act_quant, no bias")
     block["vendor_bf16"] = vendor
+    block["cold_ms"] = None if cold is None else round(cold, 5)
     del a, a_s, b, b_s, c
     return block
 
@@ -512,7 +548,7 @@ def bench_latency(mx, synth, torch, dev_u8, dev_bf16, stream, epilogues=False):
     10 times: launch overhead amortized) and `cold_ms` (median of 10 single launches, each after
     512 MB were written to evict the caches; events around the GEMM alone)."""
     res = {}
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
 
     def graph_ms(launch, reps=20, iters=10):
         g = torch.cuda.CUDAGraph()
@@ -529,19 +565,6 @@ def bench_latency(mx, synth, torch, dev_u8, dev_bf16, stream, epilogues=False):
         end.record(cur)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / (iters * reps)
-
-    def cold_ms(launch, iters=10):
-        cur = torch.cuda.current_stream()
-        ts = []
-        for i in range(iters):
-            flush.fill_(i & 0xFF)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(cur)
-            launch(stream)
-            b.record(cur)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        return statistics.median(ts)
 
     def run(w, kind, hbm=False):
         if w.a_kind == "acts":
@@ -563,7 +586,10 @@ def bench_latency(mx, synth, torch, dev_u8, dev_bf16, stream, epilogues=False):
         ms, _, _ = timed(lambda: launch(stream), torch)
         flops = 2.0 * w.M * w.N * w.K
         r = {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
-             "graph_ms": round(graph_ms(launch), 5), "cold_ms": round(cold_ms(launch), 5)}
+             "graph_ms": round(graph_ms(launch), 5),
+             "cold_ms": cold_ms(lambda: launch(stream), torch, flush)}
+        if r["cold_ms"] is not None:
+            r["cold_ms"] = round(r["cold_ms"], 5)
         r["graph_tflops"] = round(flops / (r["graph_ms"] * 1e-3) / 1e12, 3)
         if hbm:
             nbytes = (w.M * w.K / 2 + w.M * w.K / 32 + w.N * w.K / 2 + w.N * w.K / 32 +
@@ -571,7 +597,8 @@ def bench_latency(mx, synth, torch, dev_u8, dev_bf16, stream, epilogues=False):
             r["algorithmic_bytes"] = nbytes
             r["gbs"] = round(nbytes / (r["ms"] * 1e-3) / 1e9, 1)
             r["graph_gbs"] = round(nbytes / (r["graph_ms"] * 1e-3) / 1e9, 1)
-            r["cold_gbs"] = round(nbytes / (r["cold_ms"] * 1e-3) / 1e9, 1)
+            r["cold_gbs"] = (None if r["cold_ms"] is None else
+                             round(nbytes / (r["cold_ms"] * 1e-3) / 1e9, 1))
             r["graph_frac_of_hbm"] = round(r["graph_gbs"] / HBM_PEAK_GBS, 4)
         if epilogues and kind == "fp4_fp4":
             r.update(bench_a4w4_epilogues(mx, torch, a, a_s, b, b_s, bias_t, c, w, kind, stream))
