@@ -293,10 +293,11 @@ def cpu_baseline(w, rows: int, min_seconds: float = 10.0, max_runs: int = 30):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    runs, total = 0, 0.0
+    runs, total, aq_total = 0, 0.0, 0.0
     while runs < max_runs and (runs == 0 or total < min_seconds):
         t0 = time.perf_counter()
         codes, sb = O.act_quant(w.x[:rows])
+        aq_total += time.perf_counter() - t0
         A = O.decode_e4m3_rows(codes, sb)
         B = O.decode_fp4_rows(w.b, w.b_s)
         ref, S = O.gemm_ref(A, B, O.bf16_to_f64(w.bias))
@@ -305,8 +306,13 @@ def cpu_baseline(w, rows: int, min_seconds: float = 10.0, max_runs: int = 30):
         del codes, sb, A, B, ref, S
     dt = total / runs
     flops = 2.0 * rows * w.N * w.K
+    aq_bytes = ACT_QUANT_BYTES_PER_ELEM * rows * w.K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3), "runs": runs,
+            "act_quant_gbs": round(aq_bytes / (aq_total / runs) / 1e9, 4),
+            "act_quant_note": f"the oracle's act_quant alone on the same rows (numpy, one thread), "
+                              f"{ACT_QUANT_BYTES_PER_ELEM} algorithmic bytes per element, mean "
+                              f"over the same runs",
             "sample": f"act_quant + decode + float64 GEMM (with sum|a*b|) for rows 0..{rows - 1} of "
                       f"A [4096, 2048] against all 7168 weight rows, repeated {runs} times "
                       f"({total:.1f} s in all); flops counted as 2*{rows}*N*K per run"}
